@@ -1,0 +1,197 @@
+/*
+ * moe.h - C ABI of a single MoE feed-forward layer's forward pass on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page 3, "跟随一个Token走完路由、分发、专家计算到合并和多机放置的整条路径",
+ * m.lsln.cn/news/228042, section "MoE层的结构与token路由") is
+ *
+ *     y(x) = sum over e in S(x) of w_e(x) * E_e(x)
+ *
+ * where S(x) is the set of experts the router selects for token x, w_e(x)
+ * their routing weights and E_e expert e. The steps follow the same page's
+ * section "单机MoE执行流水线" (single-GPU pipeline): router scores, top-k,
+ * permute token rows into one contiguous block per expert while recording an
+ * inverse map, the grouped GEMM with the activation and the output
+ * projection, then restore token order, apply the weights and accumulate.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer unless stated otherwise,
+ *   allocated and owned by the caller. The library never allocates, frees or
+ *   synchronises; each call only enqueues kernels on `stream` and returns.
+ * - Row-major layouts: x[T,H], Wr[H,E], W1[E,H,F], W2[E,F,H], W1s[H,Fs],
+ *   W2s[Fs,H]. T tokens, H hidden width, F expert hidden width, E routed
+ *   experts, k experts per token, Fs shared-expert hidden width.
+ * - `dt` is the type of x, Wr and the expert weights: MOE_F32 (fp32
+ *   arithmetic throughout) or MOE_BF16 (bf16 operands on the matrix cores,
+ *   fp32 accumulation). Router logits, routing weights, the router bias,
+ *   y_perm and y_shared are always fp32. The intermediate expert activation
+ *   h is held in `dt`.
+ * - Slots: topk_ids[t*k + j] lists the k experts of token t in ascending
+ *   expert id; topk_w holds their weights. A slot removed by the drop
+ *   threshold keeps its expert id and has weight exactly 0.0f; a kept slot
+ *   always has a weight > 0. Dropped slots are not dispatched.
+ * - Rows of the permuted matrices are ordered by (expert id, token id), so
+ *   expert e owns rows [expert_offsets[e], expert_offsets[e+1]) and the
+ *   result is unique and reproducible (no atomics decide any order).
+ * - The number of kept assignments A = expert_offsets[E] <= T*k stays on the
+ *   device. Buffers with a row per assignment have capacity T*k rows; rows at
+ *   or after A are left untouched.
+ * - Size limits, checked before anything is launched (MOE_ERR_UNSUPPORTED):
+ *   H % 8 == 0 and F % 8 == 0 (16-byte rows), E <= 1024, k <= 32,
+ *   T*k < 2^31, and for the shared expert Fs % 8 == 0.
+ *
+ * Errors: a call returns MOE_OK after enqueueing its kernels. Argument
+ * errors return a negative status and enqueue nothing: bad sizes
+ * (T, H, F, E < 1; k < 1 or k > E), a null required pointer, drop_thresh
+ * outside [0, 1/k], an unknown dtype, or a workspace smaller than required.
+ * A failed launch returns MOE_ERR_HIP. Faults inside kernels surface at the
+ * caller's next synchronisation of `stream`.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,
+    MOE_ERR_UNSUPPORTED = -2,
+    MOE_ERR_WORKSPACE = -3,
+    MOE_ERR_HIP = -4
+} moe_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_strerror(int status);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* moe_version(void);
+
+/*
+ * Bytes of device workspace that moe_forward needs for these sizes (Fs = 0:
+ * no shared expert). It also covers moe_permute and moe_grouped_ffn, whose
+ * own needs are moe_permute_workspace_bytes and moe_ffn_workspace_bytes.
+ * Returns 0 for sizes the library rejects. Host-only; no device access.
+ */
+size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt);
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+size_t moe_ffn_workspace_bytes(int T, int F, int E, int k, int Fs, moe_dtype_t dt);
+
+/*
+ * moe_route - router logits, top-k, softmax weights, optional drop.
+ *
+ * Page 1 ("MoE大模型的智能调度…", www.jsqmd.com/news/1091713), section 2.2,
+ * routing layer: the router scores each expert, the top-k logits are turned
+ * into weights by a softmax, and a weight under the threshold (0.05 there)
+ * is zeroed before the rest are renormalised. Page 3, section
+ * "单机MoE执行流水线": top-k keeps the chosen expert indices and weights.
+ *
+ *   logits[t,e] = sum_h x[t,h] * Wr[h,e] + bias[e]       (fp32)
+ *   S_t         = k largest logits, ties to the lower expert id
+ *   w           = softmax over S_t; if drop_thresh > 0, every w < drop_thresh
+ *                 is set to 0 and the survivors are divided by their sum
+ *
+ * x: [T,H] dt. Wr: [H,E] dt. bias: [E] fp32 or NULL (zero).
+ * drop_thresh: 0 disables the drop; otherwise in (0, 1/k].
+ * Out: topk_ids [T,k] int32, topk_w [T,k] fp32 (slot order: ascending id).
+ */
+int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
+              float drop_thresh, moe_dtype_t dt, int32_t* topk_ids, float* topk_w,
+              hipStream_t stream);
+
+/*
+ * moe_permute - dispatch: group the kept assignments by expert.
+ *
+ * Page 3, section "一个批次如何变成各专家专属的矩阵": each assignment carries a
+ * token vector, an expert and a weight; assignments are grouped per expert
+ * into matrices and the source token id is kept beside every row. Section
+ * "单机MoE执行流水线": the permute reads token vectors, writes them in expert
+ * order and records an inverse map for the combine.
+ *
+ * In:  x [T,H] dt; topk_ids, topk_w [T,k] as written by moe_route.
+ * Out: x_perm [T*k, H] dt       x_perm[r] = x[row_token[r]]
+ *      expert_offsets [E+1]     exclusive prefix sum of per-expert counts
+ *      row_token [T*k]          source token of row r (r < A)
+ *      inv [T*k]                inv[t*k+j] = row of slot j of token t, -1 if dropped
+ * ws: device workspace of at least moe_permute_workspace_bytes(T,E,k) bytes.
+ */
+int moe_permute(const void* x, const int32_t* topk_ids, const float* topk_w, int T, int H, int E,
+                int k, moe_dtype_t dt, void* x_perm, int32_t* expert_offsets, int32_t* row_token,
+                int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_ffn - every expert's two-layer FFN over its rows, one ragged
+ * launch per layer.
+ *
+ * Page 1, section 2.2, expert layer: each expert is an independent two-layer
+ * FFN with its own W1, W2. Page 3, section "单机MoE执行流水线": a grouped
+ * GEMM runs several expert matrices with different row counts in one kernel
+ * launch; the experts then apply their activation and output projection.
+ *
+ *   for each expert e and row r in [expert_offsets[e], expert_offsets[e+1]):
+ *     h[r]      = silu(x_perm[r] @ W1[e])        silu(u) = u / (1 + exp(-u))
+ *     y_perm[r] = h[r] @ W2[e]                   (fp32 out)
+ *
+ * Optional shared expert (page 3, section "MoE层的结构与token路由": a shared
+ * expert is not scored by the router and every token passes through it):
+ * when W1s != NULL, also y_shared[t] = silu(x[t] @ W1s) @ W2s for all t.
+ *
+ * x_perm [T*k,H] dt; expert_offsets [E+1] on the device; W1 [E,H,F];
+ * W2 [E,F,H]; y_perm [T*k,H] fp32. x [T,H] dt, W1s [H,Fs], W2s [Fs,H] and
+ * y_shared [T,H] fp32 are needed only with the shared expert (else NULL, Fs=0).
+ * ws: at least moe_ffn_workspace_bytes(T,F,E,k,Fs,dt) bytes (holds h).
+ */
+int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const void* W1,
+                    const void* W2, int T, int H, int F, int E, int k, moe_dtype_t dt,
+                    float* y_perm, const void* x, const void* W1s, const void* W2s, int Fs,
+                    float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine - unpermute and route-weight combine.
+ *
+ * Page 1, section 2.2, fusion layer: the output is the gate-weighted sum of
+ * the chosen experts' outputs. Page 3, section "一个批次如何变成各专家专属的矩阵":
+ * a token's results are scaled by their weights and added; section
+ * "单机MoE执行流水线": the inverse map restores token order first.
+ *
+ *   y[t] = sum_{j: inv[t*k+j] >= 0} topk_w[t*k+j] * y_perm[inv[t*k+j]]  (+ y_shared[t])
+ *
+ * accumulated in fp32 in slot order, then written as out_dt (MOE_F32 keeps
+ * the accumulator; MOE_BF16 rounds it to nearest even).
+ * y_perm [T*k,H] fp32; inv, topk_w [T,k]; y_shared [T,H] fp32 or NULL;
+ * y [T,H] out_dt.
+ */
+int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w,
+                const float* y_shared, int T, int H, int k, moe_dtype_t out_dt, void* y,
+                hipStream_t stream);
+
+/*
+ * moe_forward - the whole layer: moe_route, moe_permute, moe_grouped_ffn
+ * (with the shared expert when W1s != NULL) and moe_combine, enqueued on one
+ * stream with no host synchronisation in between.
+ *
+ * y [T,H] out_dt. The debug outputs topk_ids, topk_w [T,k], expert_offsets
+ * [E+1] and inv [T,k] may be NULL; when given they receive the same values
+ * the step-wise calls would produce. ws: at least
+ * moe_workspace_bytes(T,H,F,E,k,Fs,dt) bytes.
+ */
+int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1, const void* W2,
+                const void* W1s, const void* W2s, int Fs, int T, int H, int F, int E, int k,
+                float drop_thresh, moe_dtype_t dt, void* y, moe_dtype_t out_dt,
+                int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* inv,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */
