@@ -1,0 +1,232 @@
+"""Benchmark of the single-GPU MoE-layer forward (route, permute, grouped FFN, combine).
+
+One step = one moe_forward over the whole prefill batch (T=8192 tokens,
+H=2048, F=768, E=128 routed experts, top-8, bf16 operands, fp32 accumulation),
+inputs resident in HBM. Prints ONE JSON line with the layer's tokens/s, the
+grouped FFN's MFMA roofline fraction, per-stage times, the decode-shaped layer
+(T=32) next to it, and the fp64 CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def event_time_ms(fn, reps, stream):
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    fn()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def stage_times(d, I, reps):
+    """Per-stage HIP-event times (ms) through the step-wise C-ABI calls, on the current stream."""
+    import torch
+
+    import top_routing_grouped_gemm_amd as moe
+
+    s = torch.cuda.current_stream()
+    T, k, E, H, F = I.T, I.k, I.E, I.H, I.F
+    dev = d["x"].device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    x_perm = torch.empty((T * k, H), dtype=d["x"].dtype, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+    pws = torch.empty(moe.moe_permute_workspace_bytes(T, E, k), dtype=torch.uint8, device=dev)
+    fws = torch.empty(moe.moe_ffn_workspace_bytes(T, F, E, k, I.Fs, d["x"].dtype), dtype=torch.uint8, device=dev)
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def route():
+        moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop, topk_ids=ids, topk_w=w)
+
+    def permute():
+        moe.moe_permute(d["x"], ids, w, E, x_perm=x_perm, expert_offsets=off, row_token=row_token, inv=inv, ws=pws)
+
+    def ffn():
+        moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm, ws=fws)
+
+    def combine():
+        moe.moe_combine(y_perm, inv, w, y=y)
+
+    route()
+    permute()
+    torch.cuda.synchronize()
+    A = int(off[-1].item())
+    counts = (off[1:] - off[:-1]).cpu()
+    out = {name: event_time_ms(fn, reps, s) for name, fn in
+           (("route", route), ("permute", permute), ("grouped_ffn", ffn), ("combine", combine))}
+    return out, A, counts
+
+
+def bytes_model(I, A, experts_hit):
+    """Algorithmic HBM bytes per call of each stage (each array read or written once)."""
+    b = I.elem_bytes
+    T, H, F, E, k = I.T, I.H, I.F, I.E, I.k
+    return {
+        "route": T * H * b + H * E * b + T * k * 8,
+        "permute": T * H * b + A * H * b + T * k * 8 * 2 + A * 4,
+        "grouped_ffn": experts_hit * 2 * H * F * b + A * H * b + A * H * 4,
+        "combine": A * H * 4 + T * k * 8 + T * H * 4,
+    }
+
+
+def run_workload(name, steps, warmup, stage_reps):
+    import numpy as np
+    import torch
+
+    import gen
+    import top_routing_grouped_gemm_amd as moe
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    I = gen.make_inputs(name)
+    d = gen.to_device(I, dev)
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
+    ws = torch.empty(moe.moe_workspace_bytes(I.T, I.H, I.F, I.E, I.k, I.Fs, d["x"].dtype), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty((I.T, I.H), dtype=torch.float32, device=dev)
+
+    def step():
+        moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], I.k, I.drop, W1s=d["W1s"], W2s=d["W2s"], y=y,
+                        ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3 / steps
+    st, A, counts = stage_times(d, I, stage_reps)
+    hit = int((counts > 0).sum())
+    flops = 4.0 * A * I.H * I.F
+    byts = bytes_model(I, A, hit)
+    res = {
+        "T": I.T, "H": I.H, "F": I.F, "E": I.E, "k": I.k, "A": A, "experts_hit": hit,
+        "rows_per_expert": {"min": int(counts.min()), "max": int(counts.max()),
+                            "mean": float(counts.float().mean())},
+        "ms_per_step": ms, "tokens_per_s": I.T / (ms * 1e-3),
+        "stages_ms": {k: round(v, 5) for k, v in st.items()},
+        "stage_gbs": {k: round(byts[k] / (st[k] * 1e-3) / 1e9, 1) for k in st},
+        "stage_hbm_frac": {k: round(byts[k] / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k in st},
+        "grouped_ffn_tflops": flops / (st["grouped_ffn"] * 1e-3) / 1e12,
+        "grouped_ffn_flops": flops,
+        "algorithmic_bytes": byts,
+    }
+    del d, ws
+    torch.cuda.empty_cache()
+    return I, res
+
+
+def cpu_baseline(I_name):
+    """The fp64 oracle, as it stands, on the host cores over the whole prefill batch."""
+    import numpy as np
+
+    import gen
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    I = gen.make_inputs(I_name)
+    x, Wr = I.f64(I.x), I.f64(I.Wr)
+    W1, W2 = I.f64(I.W1()), I.f64(I.W2())
+    t = time.perf_counter()
+    r = oracle.forward(x, Wr, I.bias_f64(), W1, W2, I.k, I.drop)
+    dt = time.perf_counter() - t
+    return {"value": round(I.T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole {I_name} batch (T={I.T}), fp64 numpy/OpenBLAS, {dt:.1f}s",
+            "stages_s": {k: round(v, 3) for k, v in r.times.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer forward runs on a single MI355X; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import top_routing_grouped_gemm_amd as moe
+
+    moe.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    I, pre = run_workload("prefill", args.steps, args.warmup, args.stage_reps)
+    line = {
+        "metric": "MoE-layer tokens/s + grouped-GEMM % MFMA peak, E=128 top-8 prefill & decode",
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox normals, random-init router and experts)",
+        "config": {"workload": "prefill MoE layer T=8192 H=2048 F=768 E=128 top-8", "T": I.T, "H": I.H, "F": I.F,
+                   "E": I.E, "k": I.k, "parallelism": "single GPU"},
+        "roofline": {
+            "kernel": "grouped_ffn (W1+SiLU launch and W2 launch)",
+            "bound": "mfma",
+            "achieved": round(pre["grouped_ffn_tflops"], 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre["grouped_ffn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "prefill": pre,
+    }
+    if not args.no_decode:
+        Id, dec = run_workload("decode", max(args.steps, 50), args.warmup, max(args.stage_reps, 100))
+        wbytes = dec["experts_hit"] * 2 * Id.H * Id.F * Id.elem_bytes
+        dec["weight_stream_gbs"] = round(wbytes / (dec["stages_ms"]["grouped_ffn"] * 1e-3) / 1e9, 1)
+        dec["weight_stream_hbm_frac"] = round(dec["weight_stream_gbs"] / PEAK_HBM_GBS, 4)
+        line["decode"] = dec
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle) ...")
+        line["cpu_baseline"] = cpu_baseline("prefill")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -151,7 +151,8 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     global _BF16_F64
     if dtype == "bf16":
         if _BF16_F64 is None:
-            _BF16_F64 = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+            with np.errstate(invalid="ignore"):
+                _BF16_F64 = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
         return _BF16_F64[np.asarray(a, dtype=np.uint16)]
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
@@ -315,3 +316,35 @@ def make_inputs(name: str = "tiny", seed: Optional[int] = None, **over) -> MoEIn
 
     return MoEInputs(name=name, T=T, H=H, F=F, E=E, k=k, Fs=cfg.get("Fs", 0), drop=float(cfg["drop"]),
                      dtype=dt, seed=sd, x=x, Wr=Wr, bias=bias, attempts=attempts, beta=beta)
+
+
+# ------------------------------------------------------------ device upload --
+def storage_to_torch(a: np.ndarray, dtype: str):
+    """Storage array -> CPU torch tensor (bf16 bits reinterpreted as torch.bfloat16)."""
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+
+
+def to_device(I: MoEInputs, device="cuda", experts_per_chunk: Optional[int] = None) -> dict:
+    """Copy every array of a workload to `device`; expert weights are drawn and copied in chunks."""
+    import torch
+
+    tdt = torch.bfloat16 if I.dtype == "bf16" else torch.float32
+    out = {"x": storage_to_torch(I.x, I.dtype).to(device), "Wr": storage_to_torch(I.Wr, I.dtype).to(device),
+           "bias": torch.from_numpy(I.bias).to(device) if I.bias is not None else None}
+    per_expert = I.H * I.F
+    if experts_per_chunk is None:
+        experts_per_chunk = max(1, (256 << 20) // max(1, per_expert))
+    W1 = torch.empty((I.E, I.H, I.F), dtype=tdt, device=device)
+    W2 = torch.empty((I.E, I.F, I.H), dtype=tdt, device=device)
+    for e0 in range(0, I.E, experts_per_chunk):
+        e1 = min(I.E, e0 + experts_per_chunk)
+        W1[e0:e1].copy_(storage_to_torch(I.W1(e0, e1), I.dtype))
+        W2[e0:e1].copy_(storage_to_torch(I.W2(e0, e1), I.dtype))
+    out["W1"], out["W2"] = W1, W2
+    out["W1s"] = storage_to_torch(I.W1s(), I.dtype).to(device) if I.Fs else None
+    out["W2s"] = storage_to_torch(I.W2s(), I.dtype).to(device) if I.Fs else None
+    return out

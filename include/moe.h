@@ -30,7 +30,8 @@
  * - Slots: topk_ids[t*k + j] lists the k experts of token t in ascending
  *   expert id; topk_w holds their weights. A slot removed by the drop
  *   threshold keeps its expert id and has weight exactly 0.0f; a kept slot
- *   always has a weight > 0. Dropped slots are not dispatched.
+ *   always has a weight > 0. Dropped slots are not dispatched; moe_permute
+ *   also treats a slot whose id lies outside [0, E) as dropped.
  * - Rows of the permuted matrices are ordered by (expert id, token id), so
  *   expert e owns rows [expert_offsets[e], expert_offsets[e+1]) and the
  *   result is unique and reproducible (no atomics decide any order).

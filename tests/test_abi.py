@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before launching anything (no GPU needed:
+every call here returns at argument validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("top_routing_grouped_gemm_amd")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return moe.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+                          "moe_workspace_bytes", "moe_strerror"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(moe.EXPORTS) == set(names)
+
+
+def test_strerror_and_version(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert moe.strerror(st).startswith("MOE_")
+    assert "unknown" in moe.strerror(7)
+    assert re.match(r"^\d+\.\d+\.\d+$", moe.version())
+
+
+def test_workspace_queries(lib):
+    bf16, f32 = 1, 0
+    T, H, F, E, k = 8192, 2048, 768, 128, 8
+    n = lib.moe_workspace_bytes(T, H, F, E, k, 0, bf16)
+    # at least x_perm (bf16) + y_perm (fp32) + h (bf16)
+    assert n >= T * k * (H * 2 + H * 4 + F * 2)
+    assert lib.moe_workspace_bytes(T, H, F, E, k, 4096, bf16) > n  # shared expert adds h_sh, y_sh
+    assert lib.moe_workspace_bytes(T, H, F, E, k, 0, f32) > n
+    assert lib.moe_permute_workspace_bytes(T, E, k) == ((T * k + 255) // 256) * E * 4
+    assert lib.moe_ffn_workspace_bytes(T, F, E, k, 0, bf16) >= T * k * F * 2
+    for bad in [(0, H, F, E, k), (T, 0, F, E, k), (T, H, 0, E, k), (T, H, F, 0, k), (T, H, F, E, 0),
+                (T, H, F, E, E + 1), (T, 12, F, E, k), (T, H, F, 2048, k), (T, H, F, 64, 40)]:
+        assert lib.moe_workspace_bytes(*bad, 0, bf16) == 0, bad
+    assert lib.moe_workspace_bytes(T, H, F, E, k, 0, 7) == 0
+    assert lib.moe_workspace_bytes(T, H, F, E, k, 12, bf16) == 0
+
+
+def _p(v=0x1000):
+    return ctypes.c_void_p(v)  # never dereferenced: validation fails first
+
+
+def test_route_rejects(lib):
+    N = None
+    ok = dict(x=_p(), Wr=_p(), b=N, T=4, H=8, E=4, k=2, drop=0.0, dt=1, ids=_p(), w=_p(), s=N)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_route(a["x"], a["Wr"], a["b"], a["T"], a["H"], a["E"], a["k"], a["drop"], a["dt"], a["ids"],
+                             a["w"], a["s"])
+
+    assert call(T=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(k=5) == moe.MOE_ERR_INVALID_ARG
+    assert call(k=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=N) == moe.MOE_ERR_INVALID_ARG
+    assert call(ids=N) == moe.MOE_ERR_INVALID_ARG
+    assert call(drop=0.6) == moe.MOE_ERR_INVALID_ARG   # > 1/k
+    assert call(drop=-0.1) == moe.MOE_ERR_INVALID_ARG
+    assert call(drop=float("nan")) == moe.MOE_ERR_INVALID_ARG
+    assert call(dt=3) == moe.MOE_ERR_INVALID_ARG
+    assert call(H=12) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=2000, k=2) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_permute_ffn_combine_forward_reject(lib):
+    N = None
+    # permute: undersized workspace
+    need = lib.moe_permute_workspace_bytes(64, 4, 2)
+    assert lib.moe_permute(_p(), _p(), _p(), 64, 8, 4, 2, 1, _p(), _p(), _p(), _p(), _p(), need - 1, N) \
+        == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(_p(), _p(), _p(), 64, 8, 4, 2, 1, _p(), N, _p(), _p(), _p(), need, N) \
+        == moe.MOE_ERR_INVALID_ARG
+    # grouped ffn: shared expert needs all of x, W2s, y_shared; Fs multiple of 8
+    need = lib.moe_ffn_workspace_bytes(64, 16, 4, 2, 0, 1)
+    assert lib.moe_grouped_ffn(_p(), _p(), _p(), _p(), 64, 8, 16, 4, 2, 1, _p(), N, _p(), N, 8, N, _p(), need, N) \
+        == moe.MOE_ERR_INVALID_ARG
+    need_s = lib.moe_ffn_workspace_bytes(64, 16, 4, 2, 8, 1)
+    assert lib.moe_grouped_ffn(_p(), _p(), _p(), _p(), 64, 8, 16, 4, 2, 1, _p(), _p(), _p(), _p(), 12, _p(), _p(),
+                               need_s, N) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_ffn(_p(), _p(), _p(), _p(), 64, 8, 16, 4, 2, 1, _p(), _p(), _p(), _p(), 8, _p(), _p(),
+                               need, N) == moe.MOE_ERR_WORKSPACE
+    # combine
+    assert lib.moe_combine(_p(), _p(), _p(), N, 0, 8, 2, 0, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(_p(), _p(), _p(), N, 4, 6, 2, 0, _p(), N) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(_p(), N, _p(), N, 4, 8, 2, 0, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    # forward
+    need = lib.moe_workspace_bytes(64, 8, 16, 4, 2, 0, 1)
+    args = [_p(), _p(), N, _p(), _p(), N, N, 0, 64, 8, 16, 4, 2, 0.0, 1, _p(), 0, N, N, N, N, _p(), need, N]
+    bad = list(args)
+    bad[22] = need - 1
+    assert lib.moe_forward(*bad) == moe.MOE_ERR_WORKSPACE
+    bad = list(args)
+    bad[5] = _p()  # W1s without W2s
+    assert lib.moe_forward(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[13] = 0.7
+    assert lib.moe_forward(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[16] = 5
+    assert lib.moe_forward(*bad) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        moe.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: expert ids, expert offsets, row order (row_token), inverse map and the
+permuted rows are bit-exact; routing weights within 2e-6; layer output y
+within max-abs 2e-2 * rms(y_oracle) (bf16 operands, fp32 accumulation).
+Full-size workloads compare every routing array in full and y on a seeded
+sample of tokens that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from tests.test_oracle import worked_example_inputs, _golden
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("top_routing_grouped_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+
+W_TOL = 2e-6
+Y_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_steps(d, I, dev, out_dtype=torch.float32):
+    """route -> permute -> grouped_ffn -> combine through the step-wise entry points."""
+    T, k, E = I.T, I.k, I.E
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop)
+    x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, E)
+    y_perm, y_sh = moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, x=d["x"] if I.Fs else None,
+                                       W1s=d["W1s"], W2s=d["W2s"])
+    y = moe.moe_combine(y_perm, inv, w, y_sh, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return dict(ids=ids, w=w, x_perm=x_perm, off=off, row_token=row_token, inv=inv, y_perm=y_perm, y_sh=y_sh, y=y)
+
+
+def check_routing(g, ref_route, ref_disp, x_storage=None, I=None):
+    ids = g["ids"].cpu().numpy()
+    w = g["w"].cpu().numpy().astype(np.float64)
+    assert np.array_equal(ids, ref_route.ids), "expert ids differ"
+    assert np.abs(w - ref_route.w).max() <= W_TOL, "routing weights differ"
+    assert np.array_equal(w == 0.0, ~ref_route.keep), "dropped slots differ"
+    off = g["off"].cpu().numpy()
+    assert np.array_equal(off, ref_disp.offsets), "expert offsets differ"
+    A = int(off[-1])
+    assert np.array_equal(g["row_token"].cpu().numpy()[:A], ref_disp.row_token), "row order differs"
+    assert np.array_equal(g["inv"].cpu().numpy(), ref_disp.inv), "inverse map differs"
+    if x_storage is not None:
+        xp = g["x_perm"][:A].cpu()
+        xp = xp.view(torch.int16).numpy().view(np.uint16) if xp.dtype == torch.bfloat16 else xp.numpy()
+        assert np.array_equal(xp, x_storage[ref_disp.row_token]), "permuted rows differ"
+
+
+def check_y(y_gpu, y_ref, tol=Y_TOL):
+    rms = float(np.sqrt((y_ref ** 2).mean()))
+    err = float(np.abs(y_gpu - y_ref).max())
+    assert err <= tol * rms, f"max-abs error {err:.3e} > {tol} * rms {rms:.3e}"
+    return err / rms
+
+
+# ------------------------------------------------------ worked example --
+def _we_device(dev, pad_to=8):
+    x, Wr, _, k = worked_example_inputs()
+    T, E = x.shape
+    xp = np.zeros((T, pad_to), dtype=np.float32)
+    xp[:, :E] = x
+    Wrp = np.zeros((pad_to, E), dtype=np.float32)
+    Wrp[:E] = Wr
+    return torch.from_numpy(xp).to(dev), torch.from_numpy(Wrp).to(dev), k, E
+
+
+@pytest.mark.parametrize("drop", [0.0, 0.25])
+def test_worked_example(dev, drop):
+    g = _golden()
+    exp = g["derived"] if drop == 0.0 else dict(g["derived"], **g["drop_case"])
+    x, Wr, k, E = _we_device(dev)
+    ids, w = moe.moe_route(x, Wr, None, k, drop)
+    x_perm, off, row_token, inv = moe.moe_permute(x, ids, w, E)
+    torch.cuda.synchronize()
+    assert ids.cpu().tolist() == exp["topk_ids"]
+    assert np.abs(w.cpu().numpy() - np.array(exp["topk_w"])).max() <= 1e-6
+    assert off.cpu().tolist() == exp["offsets"]
+    A = exp["offsets"][-1]
+    assert row_token.cpu().tolist()[:A] == exp["row_token"]
+    assert inv.cpu().tolist() == exp["inv"]
+    # combine with unit-vector expert rows: y[t] spells out (row, weight) pairs
+    y_perm = torch.zeros((8, 8), dtype=torch.float32, device=dev)
+    y_perm[:A] = torch.eye(8, device=dev)[:A]
+    y = moe.moe_combine(y_perm, inv, w).cpu().numpy()
+    want = np.zeros((4, 8))
+    for t in range(4):
+        for j in range(2):
+            r = exp["inv"][t][j]
+            if r >= 0:
+                want[t, r] += exp["topk_w"][t][j]
+    assert np.abs(y - want).max() <= 1e-6
+
+
+# --------------------------------------------------------- small layers --
+SMALL = [
+    ("tiny", {}),
+    ("tiny", {"dtype": "bf16", "seed": 77}),
+    ("tiny", {"T": 37, "H": 64, "F": 96, "E": 8, "k": 3, "dtype": "bf16", "seed": 78}),     # ragged tails
+    ("tiny", {"T": 300, "H": 136, "F": 200, "E": 16, "k": 4, "dtype": "bf16", "seed": 79}),
+    ("tiny", {"T": 200, "H": 128, "F": 136, "E": 6, "k": 2, "dtype": "bf16", "seed": 80, "drop": 0.3,
+              "zipf": 1.2}),
+    ("tiny", {"T": 1, "H": 64, "F": 64, "E": 8, "k": 2, "dtype": "bf16", "seed": 81}),      # one token
+    ("tiny", {"T": 50, "H": 64, "F": 64, "E": 5, "k": 5, "dtype": "f32", "seed": 82}),      # k == E
+    ("tiny", {"T": 40, "H": 64, "F": 64, "E": 1, "k": 1, "dtype": "bf16", "seed": 83}),     # single expert
+    ("tiny", {"T": 64, "H": 64, "F": 128, "E": 4, "k": 2, "dtype": "bf16", "seed": 84, "Fs": 64}),  # shared
+    ("tiny", {"T": 90, "H": 72, "F": 40, "E": 12, "k": 2, "dtype": "f32", "seed": 85, "Fs": 24, "drop": 0.2}),
+    ("tiny", {"T": 520, "H": 64, "F": 64, "E": 300, "k": 6, "dtype": "bf16", "seed": 86}),  # E > 256, E%8 != 0 rows
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_small_layers(dev, name, over):
+    I = gen.make_inputs(name, **over)
+    _say(f"case {name} {over}")
+    d = gen.to_device(I, dev)
+    g = run_steps(d, I, dev)
+    W1s, W2s = I.f64(I.W1s()), I.f64(I.W2s())
+    ref = oracle.forward(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.f64(I.W1()), I.f64(I.W2()), I.k, I.drop, W1s, W2s)
+    check_routing(g, ref.route, ref.dispatch, I.x)
+    A = int(ref.dispatch.offsets[-1])
+    check_y(g["y_perm"][:A].double().cpu().numpy(), ref.y_perm)
+    check_y(g["y"].double().cpu().numpy(), ref.y)
+    # the one-call path gives bit-identical results
+    y2 = moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], I.k, I.drop, W1s=d["W1s"], W2s=d["W2s"])
+    torch.cuda.synchronize()
+    assert torch.equal(y2, g["y"])
+
+
+def test_router_odd_expert_count(dev):
+    """E % 8 != 0 takes the scalar Wr path of the bf16 router."""
+    I = gen.make_inputs("tiny", T=70, H=64, F=64, E=13, k=3, dtype="bf16", seed=90)
+    d = gen.to_device(I, dev)
+    ids, w = moe.moe_route(d["x"], d["Wr"], None, I.k)
+    torch.cuda.synchronize()
+    r = oracle.route(I.f64(I.x), I.f64(I.Wr), None, I.k)
+    assert np.array_equal(ids.cpu().numpy(), r.ids)
+    assert np.abs(w.cpu().numpy() - r.w).max() <= W_TOL
+
+
+# ------------------------------------------------- stage tests, ragged --
+@pytest.mark.parametrize("counts", [
+    [0, 1, 16, 17, 0, 64, 65, 128, 129, 3],      # empty, 1 row, tile edges of every tile shape
+    [0, 0, 0, 700, 0],                           # all rows to one expert
+    [1] * 40,                                    # decode-like: one row per expert
+    [0, 0, 0, 0, 0, 0, 0, 5],                    # only the last expert
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_grouped_ffn_ragged(dev, counts, dtype):
+    """Oracle-fed grouped FFN: x_perm and offsets built on the host, y_perm vs the oracle's grouped FFN."""
+    E = len(counts)
+    A = sum(counts)
+    H, F = 72, 136
+    seed = 500 + A + E
+    x = gen.normal(seed, 1, A * H, 1.0, dtype).reshape(A, H)
+    W1 = gen.normal(seed, 3, E * H * F, 1 / np.sqrt(H), dtype).reshape(E, H, F)
+    W2 = gen.normal(seed, 4, E * F * H, 1 / np.sqrt(F), dtype).reshape(E, F, H)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    k = 1
+    T = A  # capacity rows = T*k
+    tx = gen.storage_to_torch(x, dtype).to(dev)
+    tW1 = gen.storage_to_torch(W1, dtype).to(dev)
+    tW2 = gen.storage_to_torch(W2, dtype).to(dev)
+    toff = torch.from_numpy(off).to(dev)
+    y_perm, _ = moe.moe_grouped_ffn(tx, toff, tW1, tW2, T, k)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_ffn(gen.to_f64(x, dtype), off, gen.to_f64(W1, dtype), gen.to_f64(W2, dtype))
+    check_y(y_perm.double().cpu().numpy(), ref)
+
+
+def test_combine_oracle_fed(dev):
+    """Oracle-fed combine: inv, weights and y_perm from the oracle; y must match to fp32 rounding."""
+    I = gen.make_inputs("tiny", T=123, H=64, F=32, E=9, k=3, dtype="f32", seed=91, drop=0.2)
+    ref = oracle.forward(I.f64(I.x), I.f64(I.Wr), None, I.f64(I.W1()), I.f64(I.W2()), I.k, I.drop)
+    A = int(ref.dispatch.offsets[-1])
+    yp = torch.zeros((I.T * I.k, I.H), dtype=torch.float32)
+    yp[:A] = torch.from_numpy(ref.y_perm)
+    y = moe.moe_combine(yp.to(dev), torch.from_numpy(ref.dispatch.inv.astype(np.int32)).to(dev),
+                        torch.from_numpy(ref.route.w.astype(np.float32)).to(dev))
+    torch.cuda.synchronize()
+    assert np.abs(y.double().cpu().numpy() - ref.y).max() <= 1e-5 * np.abs(ref.y).max()
+
+
+def test_permute_oracle_fed(dev):
+    """Oracle-fed permute: ids/weights from the oracle (with drops)."""
+    I = gen.make_inputs("tiny", T=777, H=64, F=32, E=37, k=4, dtype="bf16", seed=92, drop=0.1)
+    r = oracle.route(I.f64(I.x), I.f64(I.Wr), None, I.k, I.drop)
+    dref = oracle.dispatch(r.ids, r.keep, I.E)
+    x = gen.storage_to_torch(I.x, "bf16").to(dev)
+    ids = torch.from_numpy(r.ids.astype(np.int32)).to(dev)
+    w = torch.from_numpy(r.w.astype(np.float32)).to(dev)
+    x_perm, off, row_token, inv = moe.moe_permute(x, ids, w, I.E)
+    torch.cuda.synchronize()
+    g = dict(ids=ids, w=w, off=off, row_token=row_token, inv=inv, x_perm=x_perm)
+    check_routing(g, r, dref, I.x)
+
+
+def test_bf16_output_and_determinism(dev):
+    I = gen.make_inputs("tiny", T=256, H=128, F=64, E=16, k=4, dtype="bf16", seed=93)
+    d = gen.to_device(I, dev)
+    a = moe.moe_forward(d["x"], d["Wr"], None, d["W1"], d["W2"], I.k)
+    b = moe.moe_forward(d["x"], d["Wr"], None, d["W1"], d["W2"], I.k)
+    c = moe.moe_forward(d["x"], d["Wr"], None, d["W1"], d["W2"], I.k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)  # bit-identical reruns
+    assert torch.equal(c, a.to(torch.bfloat16))  # bf16 output = RNE of the fp32 accumulator
+
+
+# ------------------------------------------------------ full workloads --
+def _sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("name,nsample", [("decode", 32), ("prefill", 48), ("mixtral_shared", 24), ("skew", 24)])
+def test_full_workload(dev, name, nsample):
+    I = gen.make_inputs(name)
+    _say(f"case {name}: T={I.T} H={I.H} F={I.F} E={I.E} k={I.k} Fs={I.Fs} drop={I.drop}")
+    d = gen.to_device(I, dev)
+    ids = torch.empty((I.T, I.k), dtype=torch.int32, device=dev)
+    w = torch.empty((I.T, I.k), dtype=torch.float32, device=dev)
+    y = moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], I.k, I.drop, W1s=d["W1s"], W2s=d["W2s"],
+                        topk_ids=ids, topk_w=w)
+    g = run_steps(d, I, dev)
+    assert torch.equal(g["y"], y) and torch.equal(g["ids"], ids)
+    r = oracle.route(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.k, I.drop)
+    dref = oracle.dispatch(r.ids, r.keep, I.E)
+    check_routing(g, r, dref, I.x)
+    toks = _sample_tokens(I.T, nsample, 7)
+
+    def W1(e):
+        return I.f64(I.W1(e, e + 1)[0])
+
+    def W2(e):
+        return I.f64(I.W2(e, e + 1)[0])
+
+    _, _, _, yref = oracle.forward_tokens(toks, I.f64(I.x), I.f64(I.Wr), I.bias_f64(), W1, W2, I.k, I.drop,
+                                          I.f64(I.W1s()), I.f64(I.W2s()))
+    rel = check_y(y[torch.from_numpy(toks).to(dev)].double().cpu().numpy(), yref)
+    _say(f"{name}: routing bit-exact over {I.T} tokens; y max-abs/rms {rel:.3e} on {len(toks)} tokens")

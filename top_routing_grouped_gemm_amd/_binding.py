@@ -1,0 +1,201 @@
+"""ctypes binding of ``libmoe.so`` (declared in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels.
+torch supplies device memory and the stream. There is no CPU fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads torch's HIP runtime first, which libmoe.so then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+
+EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_permute_workspace_bytes",
+           "moe_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libmoe.so and declare its signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it first (python -m top_routing_grouped_gemm_amd.build)")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.moe_strerror.argtypes = [i32]
+    lib.moe_strerror.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_char_p
+    lib.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.moe_workspace_bytes.restype = sz
+    lib.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_permute_workspace_bytes.restype = sz
+    lib.moe_ffn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.moe_ffn_workspace_bytes.restype = sz
+    lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp]
+    lib.moe_route.restype = i32
+    lib.moe_permute.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_permute.restype = i32
+    lib.moe_grouped_ffn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, sz,
+                                    vp]
+    lib.moe_grouped_ffn.restype = i32
+    lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.moe_combine.restype = i32
+    lib.moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp, vp,
+                                vp, vp, vp, sz, vp]
+    lib.moe_forward.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().moe_strerror(int(status)).decode()
+
+
+def version() -> str:
+    return load_library().moe_version().decode()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def moe_workspace_bytes(T, H, F, E, k, Fs=0, dtype=torch.bfloat16) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load_library().moe_workspace_bytes(T, H, F, E, k, Fs, dt))
+
+
+def moe_permute_workspace_bytes(T, E, k) -> int:
+    return int(load_library().moe_permute_workspace_bytes(T, E, k))
+
+
+def moe_ffn_workspace_bytes(T, F, E, k, Fs=0, dtype=torch.bfloat16) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load_library().moe_ffn_workspace_bytes(T, F, E, k, Fs, dt))
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(x, Wr, bias, k: int, drop_thresh: float = 0.0, topk_ids=None, topk_w=None, stream=None):
+    """Router logits, top-k, softmax weights (+ drop). Returns (topk_ids [T,k] int32, topk_w [T,k] fp32)."""
+    T, H = x.shape
+    E = Wr.shape[1]
+    dev = x.device
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    st = load_library().moe_route(_ptr(x), _ptr(Wr), _ptr(bias), T, H, E, k, float(drop_thresh), _dt(x),
+                                  _ptr(topk_ids), _ptr(topk_w), _stream(stream))
+    _check(st, "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_permute(x, topk_ids, topk_w, E: int, x_perm=None, expert_offsets=None, row_token=None, inv=None, ws=None,
+                stream=None):
+    """Dispatch. Returns (x_perm [T*k,H], expert_offsets [E+1], row_token [T*k], inv [T,k])."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if expert_offsets is None else expert_offsets
+    row_token = torch.empty(T * k, dtype=torch.int32, device=dev) if row_token is None else row_token
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev) if inv is None else inv
+    need = moe_permute_workspace_bytes(T, E, k)
+    ws = _ws(need, dev) if ws is None else ws
+    st = load_library().moe_permute(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, H, E, k, _dt(x), _ptr(x_perm),
+                                    _ptr(expert_offsets), _ptr(row_token), _ptr(inv), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    _check(st, "moe_permute")
+    return x_perm, expert_offsets, row_token, inv
+
+
+def moe_grouped_ffn(x_perm, expert_offsets, W1, W2, T: int, k: int, y_perm=None, x=None, W1s=None, W2s=None,
+                    y_shared=None, ws=None, stream=None):
+    """Grouped FFN over all experts (+ shared). Returns (y_perm [T*k,H] fp32, y_shared [T,H] fp32 or None)."""
+    E, H, F = W1.shape
+    Fs = W1s.shape[1] if W1s is not None else 0
+    dev = x_perm.device
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
+    if W1s is not None and y_shared is None:
+        y_shared = torch.empty((T, H), dtype=torch.float32, device=dev)
+    need = moe_ffn_workspace_bytes(T, F, E, k, Fs, x_perm.dtype)
+    ws = _ws(need, dev) if ws is None else ws
+    st = load_library().moe_grouped_ffn(_ptr(x_perm), _ptr(expert_offsets), _ptr(W1), _ptr(W2), T, H, F, E, k,
+                                        _dt(x_perm), _ptr(y_perm), _ptr(x), _ptr(W1s), _ptr(W2s), Fs, _ptr(y_shared),
+                                        _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_grouped_ffn")
+    return y_perm, y_shared
+
+
+def moe_combine(y_perm, inv, topk_w, y_shared=None, out_dtype=torch.float32, y=None, stream=None):
+    """Unpermute + weighted sum. Returns y [T,H] in out_dtype."""
+    T, k = inv.shape
+    H = y_perm.shape[1]
+    y = torch.empty((T, H), dtype=out_dtype, device=y_perm.device) if y is None else y
+    st = load_library().moe_combine(_ptr(y_perm), _ptr(inv), _ptr(topk_w), _ptr(y_shared), T, H, k, _dt(y), _ptr(y),
+                                    _stream(stream))
+    _check(st, "moe_combine")
+    return y
+
+
+def moe_forward(x, Wr, bias, W1, W2, k: int, drop_thresh: float = 0.0, W1s=None, W2s=None, out_dtype=torch.float32,
+                y=None, topk_ids=None, topk_w=None, expert_offsets=None, inv=None, ws=None, stream=None):
+    """The whole layer. Returns y [T,H]; the optional debug tensors are filled when given."""
+    T, H = x.shape
+    E, _, F = W1.shape
+    Fs = W1s.shape[1] if W1s is not None else 0
+    dev = x.device
+    y = torch.empty((T, H), dtype=out_dtype, device=dev) if y is None else y
+    need = moe_workspace_bytes(T, H, F, E, k, Fs, x.dtype)
+    ws = _ws(need, dev) if ws is None else ws
+    st = load_library().moe_forward(_ptr(x), _ptr(Wr), _ptr(bias), _ptr(W1), _ptr(W2), _ptr(W1s), _ptr(W2s), Fs, T, H,
+                                    F, E, k, float(drop_thresh), _dt(x), _ptr(y), _dt(y), _ptr(topk_ids),
+                                    _ptr(topk_w), _ptr(expert_offsets), _ptr(inv), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    _check(st, "moe_forward")
+    return y

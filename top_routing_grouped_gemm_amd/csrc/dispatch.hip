@@ -1,0 +1,204 @@
+// Dispatch: group the kept (token, expert) assignments by expert and copy
+// token rows into one contiguous block per expert, recording the inverse map.
+//
+// Page 3 (m.lsln.cn/news/228042), section "一个批次如何变成各专家专属的矩阵":
+// assignments are grouped per expert into matrices with the source token id
+// kept beside every row, and an expert's batch counts assignments (k rows per
+// token). Section "单机MoE执行流水线": the permute reads token vectors, writes
+// them in expert order and records an inverse map for the combine.
+//
+// Order is fixed by (expert, token), never by atomics:
+//   count  - each workgroup histograms one chunk of 256 assignments in LDS;
+//   scan   - one workgroup turns the [chunk][expert] histograms into the
+//            first output row of every (chunk, expert) pair and writes the
+//            expert offsets (exclusive prefix sum of the counts);
+//   index  - each workgroup ranks its chunk's assignments within their expert
+//            (wave ballots match equal expert ids, LDS combines the 4 waves)
+//            and writes row_token and inv;
+//   copy   - many workgroups stream the token rows into x_perm with 16-byte
+//            loads and stores (HBM-bound: T*H*b read, A*H*b written).
+#include "moe_common.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMaxE = 1024;
+
+__global__ __launch_bounds__(kDispatchChunk) void count_kernel(const int32_t* __restrict__ ids,
+                                                               const float* __restrict__ w, int n_assign, int E,
+                                                               int32_t* __restrict__ partial) {
+    __shared__ int hist[kMaxE];
+    for (int e = threadIdx.x; e < E; e += kDispatchChunk) hist[e] = 0;
+    __syncthreads();
+    const int a = blockIdx.x * kDispatchChunk + threadIdx.x;
+    if (a < n_assign && w[a] != 0.0f) {
+        const int e = ids[a];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);  // order-free: only a count
+    }
+    __syncthreads();
+    int32_t* out = partial + (long)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += kDispatchChunk) out[e] = hist[e];
+}
+
+// One workgroup of 1024 threads. partial[b][e] (counts) becomes the first
+// output row of chunk b's assignments to expert e. Threads are arranged as
+// G groups of E experts; group g owns a contiguous range of chunks, so the
+// loads of a column walk are independent and can all be in flight at once.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ partial, int n_blocks, int E,
+                                                    int32_t* __restrict__ offsets) {
+    __shared__ int gs[1024];   // [G][E] per-group sums
+    __shared__ int eoff[kMaxE];
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+    const int G = (1024 / E) > 0 ? (1024 / E) : 1;
+    const int bpg = (n_blocks + G - 1) / G;
+    const int e = tid % E, g = tid / E;
+    const bool act = tid < E * G;
+    const int b0 = g * bpg, b1 = min(n_blocks, b0 + bpg);
+    if (act) {
+        int s = 0;
+        for (int b = b0; b < b1; ++b) s += partial[(long)b * E + e];
+        gs[g * E + e] = s;
+    }
+    __syncthreads();
+    int v = 0;
+    if (tid < E)
+        for (int i = 0; i < G; ++i) v += gs[i * E + tid];
+    const int incl = wave_incl_scan(v);
+    if (l == kWave - 1) wsum[wv] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int i = 0; i < wv; ++i) wbase += wsum[i];
+    const int excl = wbase + incl - v;
+    if (tid < E) {
+        eoff[tid] = excl;
+        offsets[tid] = excl;
+    }
+    if (tid == E - 1) offsets[E] = excl + v;
+    __syncthreads();
+    if (act) {
+        int run = eoff[e];
+        for (int i = 0; i < g; ++i) run += gs[i * E + e];
+        for (int b = b0; b < b1; b += 16) {
+            int c[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) c[u] = (b + u < b1) ? partial[(long)(b + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (b + u < b1) {
+                    partial[(long)(b + u) * E + e] = run;
+                    run += c[u];
+                }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kDispatchChunk) void index_kernel(const int32_t* __restrict__ ids,
+                                                               const float* __restrict__ w,
+                                                               const int32_t* __restrict__ partial, int n_assign,
+                                                               int k, int E, int ebits, int32_t* __restrict__ row_token,
+                                                               int32_t* __restrict__ inv) {
+    constexpr int NW = kDispatchChunk / kWave;
+    __shared__ int wc[NW][kMaxE];
+    const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+    for (int i = tid; i < NW * E; i += kDispatchChunk) (&wc[0][0])[(i / E) * kMaxE + (i % E)] = 0;
+    const int a = blockIdx.x * kDispatchChunk + tid;
+    const bool valid = a < n_assign;
+    const int id = valid ? ids[a] : 0;
+    const bool kept = valid && w[a] != 0.0f && (unsigned)id < (unsigned)E;  // out-of-range ids: dropped
+    const int e = kept ? id : 0;
+    // lanes of this wave holding the same expert id: AND of per-bit ballots
+    unsigned long long same = __ballot(kept);
+    for (int b = 0; b < ebits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+    }
+    const unsigned long long below = (l == 0) ? 0ull : (~0ull >> (kWave - l));
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    __syncthreads();
+    if (kept && rank == 0) wc[wv][e] = cnt;
+    __syncthreads();
+    if (valid) {
+        if (kept) {
+            int r = partial[(long)blockIdx.x * E + e] + rank;
+            for (int i = 0; i < wv; ++i) r += wc[i][e];
+            row_token[r] = a / k;
+            inv[a] = r;
+        } else {
+            inv[a] = -1;
+        }
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const u32x4* __restrict__ x,
+                                                        const int32_t* __restrict__ row_token,
+                                                        const int32_t* __restrict__ offsets, int E, int V,
+                                                        int rows_per_block, u32x4* __restrict__ out) {
+    const int A = offsets[E];
+    const long r0 = (long)blockIdx.x * rows_per_block;
+    if (r0 >= A) return;
+    const int nrows = (int)min((long)rows_per_block, (long)A - r0);
+    const int total = nrows * V;
+    for (int base = threadIdx.x; base < total; base += 256 * U) {
+        u32x4 v[U];
+        long dst[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 256;
+            dst[u] = -1;
+            if (i < total) {
+                const long r = r0 + i / V;
+                const int c = i % V;
+                const long src = (long)row_token[r] * V + c;
+                v[u] = x[src];
+                dst[u] = r * V + c;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (dst[u] >= 0) out[dst[u]] = v[u];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial, hipStream_t s) {
+    const int nb = dispatch_blocks(n_assign);
+    hipLaunchKernelGGL(count_kernel, dim3(nb), dim3(kDispatchChunk), 0, s, ids, w, n_assign, E, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(int32_t* partial, int n_blocks, int E, int32_t* offsets, hipStream_t s) {
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, partial, n_blocks, E, offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* partial, int n_assign, int k, int E,
+                        int32_t* row_token, int32_t* inv, hipStream_t s) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    const int nb = dispatch_blocks(n_assign);
+    hipLaunchKernelGGL(index_kernel, dim3(nb), dim3(kDispatchChunk), 0, s, ids, w, partial, n_assign, k, E, ebits,
+                       row_token, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
+                            int row_bytes, void* x_perm, hipStream_t s) {
+    const int V = row_bytes / 16;
+    constexpr int U = 8;
+    int rpb = (256 * U) / V;
+    if (rpb < 1) rpb = 1;
+    const int grid = (max_rows + rpb - 1) / rpb;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((copy_rows_kernel<U>), dim3(grid), dim3(256), 0, s, (const u32x4*)x, row_token, offsets, E,
+                       V, rpb, (u32x4*)x_perm);
+    return hipGetLastError();
+}
+
+}  // namespace moe

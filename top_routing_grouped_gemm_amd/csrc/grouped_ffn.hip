@@ -1,0 +1,289 @@
+// Grouped per-expert FFN: two ragged GEMM launches over all experts at once.
+//
+// Page 1 ("MoE大模型的智能调度…", www.jsqmd.com/news/1091713), section 2.2,
+// expert layer: each expert is its own two-layer FFN (W1, W2). Page 3
+// (m.lsln.cn/news/228042), section "单机MoE执行流水线": one grouped-GEMM
+// launch runs every expert matrix although their row counts differ, then the
+// experts apply the activation and the output projection; section
+// "一个批次如何变成各专家专属的矩阵": decode gives experts one or two rows,
+// prefill many.
+//
+//   up:   h[r]      = silu(x_perm[r] @ W1[e])   (SiLU fused in the epilogue)
+//   down: y_perm[r] = h[r] @ W2[e]              (fp32 out)
+//
+// Scheduling: the M-tiles of all experts form one ragged sequence (expert e
+// contributes ceil(count_e / BM) tiles); each workgroup takes one (M-tile,
+// N-tile) pair and finds its expert with a wave-parallel prefix sum over the
+// device-side offsets, so no row count ever travels to the host. The grid is
+// sized for the worst case (ceil(rows/BM) + min(E, rows) M-tiles) and
+// workgroups past the last tile exit at once.
+//
+// bf16 mainloop: 256 threads (4 waves), BM x BN x 64 tiles staged in LDS with
+// one register-prefetched stage in flight, 16x16x32 bf16 MFMA, fp32 acc.
+#include <math.h>
+
+#include "mfma_tiles.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+
+// Expert and row range of ragged M-tile `mt`. Returns false past the last tile.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int mt, int& e_out,
+                                          int& rb, int& re) {
+    const int l = lane_id();
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = l * per, e1 = min(E, e0 + per);
+    int s = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int c = offsets[e + 1] - offsets[e];
+        s += (c + BM - 1) / BM;
+    }
+    const int incl = wave_incl_scan(s);
+    const unsigned long long own = __ballot(mt < incl);
+    if (own == 0ull) return false;
+    const int L = __ffsll((long long)own) - 1;
+    int before = __shfl(incl - s, L, kWave);
+    const int eL0 = L * per, eL1 = min(E, eL0 + per);
+    int e = eL0;
+    for (; e < eL1; ++e) {
+        const int c = offsets[e + 1] - offsets[e];
+        const int tt = (c + BM - 1) / BM;
+        if (mt < before + tt) break;
+        before += tt;
+    }
+    e_out = e;
+    rb = offsets[e] + (mt - before) * BM;
+    re = offsets[e + 1];
+    return true;
+}
+
+template <int BM>
+__device__ __forceinline__ bool locate(const int32_t* __restrict__ offsets, int E, int fixed_rows, int mt, int& e,
+                                       int& rb, int& re) {
+    if (offsets == nullptr) {
+        e = 0;
+        rb = mt * BM;
+        re = fixed_rows;
+        return rb < re;
+    }
+    return find_tile<BM>(offsets, E, mt, e, rb, re);
+}
+
+enum { kEpiSiluOut = 0, kEpiF32Out = 1 };
+
+template <int BM, int BN, int BK, int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, long lda, const uint16_t* __restrict__ B, long strideB, long ldb,
+    void* __restrict__ C, long ldc, const int32_t* __restrict__ offsets, int E, int fixed_rows, int N, int K,
+    int n_tiles) {
+    constexpr int S = BK + 8;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    static_assert(WM * WN == 4, "4 waves");
+    static_assert(TM >= 1 && TN >= 1 && BK % 32 == 0, "tile shape");
+    constexpr int APT = (BM * BK / 8 + 255) / 256;
+    __shared__ __align__(16) uint16_t As[BM * S];
+    __shared__ __align__(16) uint16_t Bs[BN * S];
+
+    const int nt = blockIdx.x % n_tiles;
+    const int mt = blockIdx.x / n_tiles;
+    int e, rb, re;
+    if (!locate<BM>(offsets, E, fixed_rows, mt, e, rb, re)) return;
+    re = min(re, rb + BM);
+    const uint16_t* Be = B + (long)e * strideB;
+    const int n0 = nt * BN;
+
+    const int wave = threadIdx.x / kWave, l = lane_id();
+    const int wm = wave / WN, wn = wave % WN;
+
+    u32x4 areg[APT];
+    BTile<BK, BN, 256> breg;
+    load_a_tile_regs<BM, BK, 256>(A, lda, rb, re, K, 0, areg);
+    breg.load(Be, ldb, K, N, 0, n0);
+    store_a_tile_lds<BM, BK, 256, S>(As, areg);
+    breg.template store<S>(Bs);
+    __syncthreads();
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        const bool more = k0 + BK < K;
+        if (more) {
+            load_a_tile_regs<BM, BK, 256>(A, lda, rb, re, K, k0 + BK, areg);
+            breg.load(Be, ldb, K, N, k0 + BK, n0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *(const bf16x8*)(As + (wm * WTM + i * 16 + (l & 15)) * S + kk + (l >> 4) * 8);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *(const bf16x8*)(Bs + (wn * WTN + j * 16 + (l & 15)) * S + kk + (l >> 4) * 8);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+        if (more) {
+            store_a_tile_lds<BM, BK, 256, S>(As, areg);
+            breg.template store<S>(Bs);
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + (l & 15);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = rb + wm * WTM + i * 16 + (l >> 4) * 4 + q;
+                if (row < re && col < N) {
+                    const float v = acc[i][j][q];
+                    if (EPI == kEpiSiluOut)
+                        ((uint16_t*)C)[(long)row * ldc + col] = (uint16_t)f32_to_bf16_bits(silu_f32(v));
+                    else
+                        ((float*)C)[(long)row * ldc + col] = v;
+                }
+            }
+        }
+}
+
+// fp32 path: 32x32 tiles on plain FMA, 2x2 outputs per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __restrict__ A, long lda,
+                                                               const float* __restrict__ B, long strideB, long ldb,
+                                                               void* __restrict__ C, long ldc,
+                                                               const int32_t* __restrict__ offsets, int E,
+                                                               int fixed_rows, int N, int K, int n_tiles) {
+    constexpr int BM = 32, BN = 32, BK = 16;
+    __shared__ float As[BK][BM + 1];
+    __shared__ float Bs[BK][BN + 1];
+    const int nt = blockIdx.x % n_tiles;
+    const int mt = blockIdx.x / n_tiles;
+    int e, rb, re;
+    if (!locate<BM>(offsets, E, fixed_rows, mt, e, rb, re)) return;
+    re = min(re, rb + BM);
+    const float* Be = B + (long)e * strideB;
+    const int n0 = nt * BN;
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        for (int i = threadIdx.x; i < BK * BM; i += 256) {
+            const int m = i / BK, kk = i % BK;
+            const int r = rb + m, kg = k0 + kk;
+            As[kk][m] = (r < re && kg < K) ? A[(long)r * lda + kg] : 0.0f;
+        }
+        for (int i = threadIdx.x; i < BK * BN; i += 256) {
+            const int kk = i / BN, n = i % BN;
+            const int kg = k0 + kk, ng = n0 + n;
+            Bs[kk][n] = (kg < K && ng < N) ? Be[(long)kg * ldb + ng] : 0.0f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < BK; ++kk) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = fmaf(As[kk][ty * 2 + a], Bs[kk][tx * 2 + b], acc[a][b]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int row = rb + ty * 2 + a, col = n0 + tx * 2 + b;
+            if (row < re && col < N) {
+                float v = acc[a][b];
+                if (EPI == kEpiSiluOut) v = v / (1.0f + expf(-v));
+                ((float*)C)[(long)row * ldc + col] = v;
+            }
+        }
+}
+
+inline long max_mtiles(int bm, const int32_t* offsets, int E, int fixed_rows, int max_rows) {
+    if (offsets == nullptr) return (fixed_rows + bm - 1) / bm;
+    long groups = E < max_rows ? E : max_rows;
+    return (max_rows + bm - 1) / bm + groups;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int EPI>
+hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long ldb, void* C, long ldc,
+                    const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
+    const int n_tiles = (N + BN - 1) / BN;
+    const long grid = max_mtiles(BM, offsets, E, fixed_rows, max_rows) * n_tiles;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const uint16_t*)A, lda, (const uint16_t*)B, strideB, ldb, C, ldc, offsets, E, fixed_rows, N,
+                       K, n_tiles);
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, long strideB, long ldb, void* C,
+                        long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K,
+                        hipStream_t s) {
+    switch (cfg) {
+        case kTileM128:
+            return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                                                     max_rows, N, K, s);
+        case kTileM64:
+            return run_bf16<64, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                                                    max_rows, N, K, s);
+        default:
+            return run_bf16<16, 128, 64, 1, 4, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                                                    max_rows, N, K, s);
+    }
+}
+
+template <int EPI>
+hipError_t run_f32(const void* A, long lda, const void* B, long strideB, long ldb, void* C, long ldc,
+                   const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
+    const int n_tiles = (N + 31) / 32;
+    const long grid = max_mtiles(32, offsets, E, fixed_rows, max_rows) * n_tiles;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI>), dim3((unsigned)grid), dim3(256), 0, s, (const float*)A, lda,
+                       (const float*)B, strideB, ldb, C, ldc, offsets, E, fixed_rows, N, K, n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+TileCfg choose_tile(long rows, int groups) {
+    const long mean = groups > 0 ? rows / groups : rows;
+    if (mean >= 96) return kTileM128;
+    if (mean >= 24) return kTileM64;
+    return kTileM16;
+}
+
+hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed_rows, int max_rows, const void* W1,
+                         int H, int F, Dtype dt, void* h, TileCfg cfg, hipStream_t s) {
+    const long strideB = (offsets == nullptr) ? 0 : (long)H * F;
+    if (dt == kBF16)
+        return run_bf16_cfg<kEpiSiluOut>(cfg, A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H, s);
+    return run_f32<kEpiSiluOut>(A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H, s);
+}
+
+hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
+                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, hipStream_t s) {
+    const long strideB = (offsets == nullptr) ? 0 : (long)F * H;
+    if (dt == kBF16)
+        return run_bf16_cfg<kEpiF32Out>(cfg, h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, s);
+    return run_f32<kEpiF32Out>(h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, s);
+}
+
+}  // namespace moe

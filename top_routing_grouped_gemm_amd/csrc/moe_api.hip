@@ -1,0 +1,255 @@
+// C ABI of the MoE-layer forward (declared in include/moe.h): argument
+// checks, workspace layout and the launch sequence on the caller's stream.
+#include "moe.h"
+
+#include "moe_internal.hpp"
+
+namespace {
+
+using moe::Dtype;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxK = 32;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool valid_dtype(moe_dtype_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// Size checks shared by all entry points; F == 0 / Fs < 0 skip the checks that
+// do not apply to a call.
+int check_sizes(int T, int H, int F, int E, int k) {
+    if (T < 1 || H < 1 || E < 1 || k < 1 || k > E || F < 0) return MOE_ERR_INVALID_ARG;
+    if (E > kMaxExperts || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+    if (H % 8 != 0 || F % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_drop(float drop, int k) {
+    if (!(drop >= 0.0f)) return MOE_ERR_INVALID_ARG;  // also rejects NaN
+    if ((double)drop > (1.0 / (double)k) * (1.0 + 1e-6)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+struct FfnLayout {
+    size_t h, h_sh, total;
+};
+
+FfnLayout ffn_layout(int T, int F, int k, int Fs, moe_dtype_t dt) {
+    FfnLayout L;
+    size_t off = 0;
+    L.h = off;
+    off = align_up(off + (size_t)T * k * F * elem_bytes(dt));
+    L.h_sh = off;
+    if (Fs > 0) off = align_up(off + (size_t)T * Fs * elem_bytes(dt));
+    L.total = off;
+    return L;
+}
+
+size_t permute_bytes(int T, int E, int k) {
+    return align_up((size_t)moe::dispatch_blocks((long)T * k) * E * sizeof(int32_t));
+}
+
+struct FwdLayout {
+    size_t ids, w, offsets, inv, row_token, partial, x_perm, y_perm, y_sh, ffn, total;
+};
+
+FwdLayout fwd_layout(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) {
+    FwdLayout L;
+    const size_t TK = (size_t)T * k;
+    size_t off = 0;
+    L.ids = off;
+    off = align_up(off + TK * sizeof(int32_t));
+    L.w = off;
+    off = align_up(off + TK * sizeof(float));
+    L.offsets = off;
+    off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
+    L.inv = off;
+    off = align_up(off + TK * sizeof(int32_t));
+    L.row_token = off;
+    off = align_up(off + TK * sizeof(int32_t));
+    L.partial = off;
+    off = align_up(off + permute_bytes(T, E, k));
+    L.x_perm = off;
+    off = align_up(off + TK * H * elem_bytes(dt));
+    L.y_perm = off;
+    off = align_up(off + TK * H * sizeof(float));
+    L.y_sh = off;
+    if (Fs > 0) off = align_up(off + (size_t)T * H * sizeof(float));
+    L.ffn = off;
+    off = align_up(off + ffn_layout(T, F, k, Fs, dt).total);
+    L.total = off;
+    return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                          \
+    do {                                       \
+        hipError_t _e = (expr);                \
+        if (_e != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, int H, int E, int k,
+                    moe_dtype_t dt, void* x_perm, int32_t* offsets, int32_t* row_token, int32_t* inv,
+                    int32_t* partial, hipStream_t s) {
+    const int n = T * k;
+    MOE_TRY(moe::launch_count(ids, w, n, E, partial, s));
+    MOE_TRY(moe::launch_scan(partial, moe::dispatch_blocks(n), E, offsets, s));
+    MOE_TRY(moe::launch_index(ids, w, partial, n, k, E, row_token, inv, s));
+    MOE_TRY(moe::launch_copy_rows(x, row_token, offsets, E, n, (int)(H * elem_bytes(dt)), x_perm, s));
+    return MOE_OK;
+}
+
+int enqueue_ffn(const void* x_perm, const int32_t* offsets, const void* W1, const void* W2, int T, int H, int F,
+                int E, int k, moe_dtype_t dt, float* y_perm, const void* x, const void* W1s, const void* W2s,
+                int Fs, float* y_shared, void* ws, hipStream_t s) {
+    const FfnLayout L = ffn_layout(T, F, k, Fs, dt);
+    char* base = (char*)ws;
+    void* h = base + L.h;
+    const Dtype d = (Dtype)dt;
+    const int rows = T * k;
+    const moe::TileCfg cfg = moe::choose_tile(rows, E);
+    MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, s));
+    if (W1s != nullptr) {
+        void* hs = base + L.h_sh;
+        const moe::TileCfg cs = moe::choose_tile(T, 1);
+        MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, s));
+        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, s));
+        MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, s));
+    } else {
+        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, s));
+    }
+    return MOE_OK;
+}
+
+int check_shared(const void* x, const void* W1s, const void* W2s, int Fs, const float* y_shared) {
+    if (W1s == nullptr && W2s == nullptr) return MOE_OK;
+    if (W1s == nullptr || W2s == nullptr || x == nullptr || y_shared == nullptr) return MOE_ERR_INVALID_ARG;
+    if (Fs < 1) return MOE_ERR_INVALID_ARG;
+    if (Fs % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: a size, pointer, threshold or dtype is invalid";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: sizes outside the supported limits";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than required";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+        default: return "unknown moe status";
+    }
+}
+
+const char* moe_version(void) { return "0.1.0"; }
+
+size_t moe_permute_workspace_bytes(int T, int E, int k) {
+    if (check_sizes(T, 8, 0, E, k) != MOE_OK) return 0;
+    return permute_bytes(T, E, k);
+}
+
+size_t moe_ffn_workspace_bytes(int T, int F, int E, int k, int Fs, moe_dtype_t dt) {
+    if (!valid_dtype(dt) || check_sizes(T, 8, F, E, k) != MOE_OK || F < 1 || Fs < 0 || Fs % 8 != 0) return 0;
+    return ffn_layout(T, F, k, Fs, dt).total;
+}
+
+size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) {
+    if (!valid_dtype(dt) || check_sizes(T, H, F, E, k) != MOE_OK || F < 1 || Fs < 0 || Fs % 8 != 0) return 0;
+    return fwd_layout(T, H, F, E, k, Fs, dt).total;
+}
+
+int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k, float drop_thresh,
+              moe_dtype_t dt, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, 0, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, topk_ids, topk_w, stream));
+}
+
+int moe_permute(const void* x, const int32_t* topk_ids, const float* topk_w, int T, int H, int E, int k,
+                moe_dtype_t dt, void* x_perm, int32_t* expert_offsets, int32_t* row_token, int32_t* inv, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, 0, E, k);
+    if (st != MOE_OK) return st;
+    if (!x || !topk_ids || !topk_w || !x_perm || !expert_offsets || !row_token || !inv || !ws)
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < permute_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+    return enqueue_permute(x, topk_ids, topk_w, T, H, E, k, dt, x_perm, expert_offsets, row_token, inv,
+                           (int32_t*)ws, stream);
+}
+
+int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const void* W1, const void* W2, int T, int H,
+                    int F, int E, int k, moe_dtype_t dt, float* y_perm, const void* x, const void* W1s,
+                    const void* W2s, int Fs, float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_shared(x, W1s, W2s, Fs, y_shared)) != MOE_OK) return st;
+    if (!x_perm || !expert_offsets || !W1 || !W2 || !y_perm || !ws) return MOE_ERR_INVALID_ARG;
+    const int fs = W1s ? Fs : 0;
+    if (ws_bytes < ffn_layout(T, F, k, fs, dt).total) return MOE_ERR_WORKSPACE;
+    return enqueue_ffn(x_perm, expert_offsets, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_shared, ws,
+                       stream);
+}
+
+int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, const float* y_shared, int T, int H,
+                int k, moe_dtype_t out_dt, void* y, hipStream_t stream) {
+    if (!valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;
+    if (T < 1 || H < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (H % 8 != 0 || k > kMaxK || (long long)T * k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!y_perm || !inv || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_combine(y_perm, inv, topk_w, y_shared, T, H, k, (Dtype)out_dt, y, stream));
+}
+
+int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1, const void* W2, const void* W1s,
+                const void* W2s, int Fs, int T, int H, int F, int E, int k, float drop_thresh, moe_dtype_t dt,
+                void* y, moe_dtype_t out_dt, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt) || !valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if (!x || !Wr || !W1 || !W2 || !y || !ws) return MOE_ERR_INVALID_ARG;
+    if ((W1s == nullptr) != (W2s == nullptr)) return MOE_ERR_INVALID_ARG;
+    const int fs = W1s ? Fs : 0;
+    if (W1s != nullptr) {
+        if (Fs < 1) return MOE_ERR_INVALID_ARG;
+        if (Fs % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    }
+    const FwdLayout L = fwd_layout(T, H, F, E, k, fs, dt);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + L.ids);
+    float* w = topk_w ? topk_w : (float*)(base + L.w);
+    int32_t* off = expert_offsets ? expert_offsets : (int32_t*)(base + L.offsets);
+    int32_t* iv = inv ? inv : (int32_t*)(base + L.inv);
+    int32_t* row_token = (int32_t*)(base + L.row_token);
+    int32_t* partial = (int32_t*)(base + L.partial);
+    void* x_perm = base + L.x_perm;
+    float* y_perm = (float*)(base + L.y_perm);
+    float* y_sh = fs > 0 ? (float*)(base + L.y_sh) : nullptr;
+    void* ffn_ws = base + L.ffn;
+
+    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, stream));
+    if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, off, row_token, iv, partial, stream)) != MOE_OK)
+        return st;
+    if ((st = enqueue_ffn(x_perm, off, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_sh, ffn_ws, stream)) !=
+        MOE_OK)
+        return st;
+    return hip_status(moe::launch_combine(y_perm, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+// Every launcher only enqueues work on `s` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+constexpr int kDispatchChunk = 256;  // assignments per dispatch workgroup
+
+// Ragged GEMM tile shapes, chosen on the host from the mean rows per expert.
+enum TileCfg { kTileM16 = 0, kTileM64 = 1, kTileM128 = 2 };
+
+inline int dispatch_blocks(long n_assign) { return (int)((n_assign + kDispatchChunk - 1) / kDispatchChunk); }
+
+hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
+                        float drop, Dtype dt, int32_t* ids, float* w, hipStream_t s);
+
+// Dispatch: per-chunk expert histograms -> scan -> stable ranks -> row copy.
+hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial,
+                        hipStream_t s);
+hipError_t launch_scan(int32_t* partial, int n_blocks, int E, int32_t* offsets, hipStream_t s);
+hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* partial, int n_assign, int k,
+                        int E, int32_t* row_token, int32_t* inv, hipStream_t s);
+hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32_t* offsets, int E,
+                            int max_rows, int row_bytes, void* x_perm, hipStream_t s);
+
+// Grouped FFN. Rows of group e are [offsets[e], offsets[e+1]); with offsets == NULL there
+// is a single group of rows [0, fixed_rows) (the shared expert).
+hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed_rows, int max_rows,
+                         const void* W1, int H, int F, Dtype dt, void* h, TileCfg cfg, hipStream_t s);
+hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
+                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, hipStream_t s);
+TileCfg choose_tile(long rows, int groups);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared,
+                          int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
+
+}  // namespace moe
