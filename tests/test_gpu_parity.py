@@ -122,6 +122,11 @@ SMALL = [
     ("tiny", {"T": 64, "H": 64, "F": 128, "E": 4, "k": 2, "dtype": "bf16", "seed": 84, "Fs": 64}),  # shared
     ("tiny", {"T": 90, "H": 72, "F": 40, "E": 12, "k": 2, "dtype": "f32", "seed": 85, "Fs": 24, "drop": 0.2}),
     ("tiny", {"T": 520, "H": 64, "F": 64, "E": 300, "k": 6, "dtype": "bf16", "seed": 86}),  # E > 256, E%8 != 0 rows
+    # large-tile (direct-to-LDS) path: K % 64 == 0, >= 96 rows per expert, partial N tiles
+    ("tiny", {"T": 700, "H": 128, "F": 192, "E": 5, "k": 2, "dtype": "bf16", "seed": 87}),
+    ("tiny", {"T": 300, "H": 256, "F": 320, "E": 4, "k": 2, "dtype": "bf16", "seed": 88, "Fs": 192}),
+    ("tiny", {"T": 1100, "H": 192, "F": 128, "E": 8, "k": 3, "dtype": "bf16", "seed": 89, "drop": 0.2,
+              "zipf": 1.2}),
 ]
 
 
@@ -160,13 +165,13 @@ def test_router_odd_expert_count(dev):
     [0, 0, 0, 700, 0],                           # all rows to one expert
     [1] * 40,                                    # decode-like: one row per expert
     [0, 0, 0, 0, 0, 0, 0, 5],                    # only the last expert
+    [130, 0, 257, 1, 128, 129, 0, 300],          # large tiles: 128-row edges, partial and single rows
 ])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_grouped_ffn_ragged(dev, counts, dtype):
+@pytest.mark.parametrize("dtype,H,F", [("bf16", 72, 136), ("f32", 72, 136), ("bf16", 128, 320)])
+def test_grouped_ffn_ragged(dev, counts, dtype, H, F):
     """Oracle-fed grouped FFN: x_perm and offsets built on the host, y_perm vs the oracle's grouped FFN."""
     E = len(counts)
     A = sum(counts)
-    H, F = 72, 136
     seed = 500 + A + E
     x = gen.normal(seed, 1, A * H, 1.0, dtype).reshape(A, H)
     W1 = gen.normal(seed, 3, E * H * F, 1 / np.sqrt(H), dtype).reshape(E, H, F)

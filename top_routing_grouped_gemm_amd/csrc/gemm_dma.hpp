@@ -1,0 +1,272 @@
+// Ragged grouped GEMM mainloop built on two gfx950 data paths:
+//
+//  * direct-to-LDS 16-byte global loads (global_load_lds_dwordx4): each
+//    lane's 16 bytes land at LDS base + 16 * lane, so one wave instruction
+//    fills a contiguous 1 KiB LDS chunk without touching VGPRs, and several
+//    LDS stages can be in flight at once;
+//  * the LDS transpose read ds_read_b64_tr_b16: within each 16-lane group,
+//    lane j supplies the address of a 4-element row j of a 16x4 block of
+//    16-bit values and lane i receives elements [4q + i/4][i%4], q = 0..3.
+//    With lane j pointing at B[kb + j/4][n0 + 4*(j%4)], lane i receives
+//    B[kb + q][n0 + i]: four k-consecutive values of column n0 + i, which is
+//    the k-packed B operand of v_mfma_f32_16x16x32_bf16. B tiles therefore
+//    stay n-contiguous in LDS, exactly as W1[E,H,F] and W2[E,F,H] lie in HBM.
+//
+// LDS layouts are XOR-swizzled at 16-byte granularity so that the operand
+// reads of one instruction spread over all banks:
+//   A [BM][BK=64] (128 B rows):  chunk c of row r sits at c ^ ((r >> 1) & 7)
+//   B [BK][BN]    (2*BN B rows): chunk c of row r sits at c ^ fB(r), where
+//                 fB(r) = 2 * ((r & 3) + 4 * ((r >> 3) & 1)) keeps 32-byte
+//                 pairs together and separates the rows one read touches.
+// The loader applies the inverse permutation to the global addresses it
+// fetches, so every global row segment is still read contiguously.
+//
+// Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin,
+// so workgroup b runs on XCD b % 8; the ragged tile sequence (experts in
+// order, M-tiles of an expert in order, N-tiles fastest) is cut into 8
+// contiguous chunks and XCD x walks chunk x. Workgroups that share an
+// expert's weight slab or an A tile then share one L2.
+#pragma once
+
+#include "moe_common.hpp"
+
+namespace moe {
+namespace dma {
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+constexpr int kXcds = 8;
+
+// s_waitcnt immediate that waits for vmcnt <= n and leaves the other counters free (gfx9 encoding).
+template <int N>
+struct VmWait {
+    static constexpr int value = (N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14);
+};
+
+// One direct-to-LDS 16-byte load per lane: lane i's 16 bytes from `src` land
+// at LDS byte address lds_base + 16 * i (lds_base wave-uniform, via M0).
+// Issued from inline asm so that the compiler does not track it as an LDS
+// write: the kernel orders it with its own s_waitcnt vmcnt + s_barrier, and
+// the main loop has no other vector-memory operation whose waits it could
+// disturb (vmcnt decrements in issue order, so extra loads in flight only
+// make any compiler-placed wait stricter).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz_b(int row, int chunk) { return chunk ^ (2 * ((row & 3) + 4 * ((row >> 3) & 1))); }
+
+// Map this workgroup to (expert, M-tile rows, N-tile). All waves compute the
+// same answer; returns false for workgroups past the last tile.
+template <int BM>
+__device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, int E, int fixed_rows, int n_tiles,
+                                         int& e_out, int& rb, int& re, int& nt) {
+    const int l = lane_id();
+    int total_m, incl = 0, s = 0, per = 1;
+    if (offsets == nullptr) {
+        total_m = (fixed_rows + BM - 1) / BM;
+    } else {
+        per = (E + kWave - 1) / kWave;
+        const int e0 = l * per, e1 = min(E, e0 + per);
+        for (int e = e0; e < e1; ++e) {
+            const int c = offsets[e + 1] - offsets[e];
+            s += (c + BM - 1) / BM;
+        }
+        incl = wave_incl_scan(s);
+        total_m = __shfl(incl, kWave - 1, kWave);
+    }
+    const long total = (long)total_m * n_tiles;
+    const long chunk = (total + kXcds - 1) / kXcds;
+    const long b = blockIdx.x;
+    if (b >= chunk * kXcds) return false;
+    const long t = (b % kXcds) * chunk + b / kXcds;
+    if (t >= total) return false;
+    const int mt = (int)(t / n_tiles);
+    nt = (int)(t % n_tiles);
+    if (offsets == nullptr) {
+        e_out = 0;
+        rb = mt * BM;
+        re = min(fixed_rows, rb + BM);
+        return true;
+    }
+    const unsigned long long own = __ballot(mt < incl);
+    const int L = __ffsll((long long)own) - 1;
+    int before = __shfl(incl - s, L, kWave);
+    const int eL0 = L * per, eL1 = min(E, eL0 + per);
+    int e = eL0;
+    for (; e < eL1; ++e) {
+        const int c = offsets[e + 1] - offsets[e];
+        const int tt = (c + BM - 1) / BM;
+        if (mt < before + tt) break;
+        before += tt;
+    }
+    e_out = e;
+    rb = offsets[e] + (mt - before) * BM;
+    re = min(offsets[e + 1], rb + BM);
+    return true;
+}
+
+// C[rows of group e, n-tile] = A[rows] @ B_e  with the fused epilogue.
+// Requirements (checked on the host): K % 64 == 0, K >= 128, N % 8 == 0, lda % 8 == 0,
+// ldb % 8 == 0.
+//
+// Pipeline: a ring of three LDS stages. k-step s waits (s_waitcnt vmcnt) for
+// its own loads, meets the other waves at a fence-free s_barrier (after which
+// every wave has landed step s and finished reading step s-1's stage),
+// starts the loads of step s+2 into that freed stage, then runs its MFMAs,
+// so two stages of loads are always in flight under the matrix work.
+template <int BM, int BN>
+struct DmaTile {
+    static constexpr int BK = 64;
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+};
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t* __restrict__ A, long lda,
+                                                          const uint16_t* __restrict__ B, long strideB, long ldb,
+                                                          void* __restrict__ C, long ldc,
+                                                          const int32_t* __restrict__ offsets, int E, int fixed_rows,
+                                                          int N, int K, int n_tiles) {
+    using Tl = DmaTile<BM, BN>;
+    constexpr int BK = Tl::BK;
+    constexpr int A_BYTES = Tl::A_BYTES;
+    constexpr int B_BYTES = Tl::B_BYTES;
+    constexpr int A_CHUNKS = A_BYTES / 1024 / 4;   // 1 KiB chunks per wave
+    constexpr int B_CHUNKS = B_BYTES / 1024 / 4;
+    constexpr int LOADS = A_CHUNKS + B_CHUNKS;     // vm ops per thread per stage
+    constexpr int B_ROW_CHUNKS = BN / 8;           // 16-byte chunks per B row
+    constexpr int B_ROWS_PER_KB = 1024 / (BN * 2);
+    constexpr int WM = 2, WN = 2;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile bytes");
+    static_assert(B_ROWS_PER_KB >= 1, "B row fits a KiB chunk");
+
+    constexpr int NS = 3;
+    __shared__ __align__(1024) uint8_t smem[NS * Tl::STAGE];
+
+    int e, rb, re, nt;
+    if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, e, rb, re, nt)) return;
+    const int n0 = nt * BN;
+    const uint16_t* Be = B + (long)e * strideB;
+
+    const int wave = threadIdx.x / kWave, l = lane_id();
+
+    // --- per-lane global source of every LDS chunk this wave fills ---------
+    const uint16_t* a_src[A_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        const int c = wave + 4 * i;               // chunk: rows 8c .. 8c+7
+        const int row = 8 * c + (l >> 3);
+        const int pos = l & 7;
+        const int kc = swz_a(row, pos);           // the XOR is its own inverse
+        const int grow = min(rb + row, re - 1);   // rows past the group repeat a valid row
+        a_src[i] = A + (long)grow * lda + kc * 8;
+    }
+    const uint16_t* b_src[B_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) {
+        const int c = wave + 4 * i;
+        const int row = c * B_ROWS_PER_KB + l / B_ROW_CHUNKS;
+        const int pos = l % B_ROW_CHUNKS;
+        const int cc = swz_b(row, pos);
+        const int col = min(n0 + cc * 8, N - 8);  // columns past N repeat a valid chunk
+        b_src[i] = Be + (long)row * ldb + col;
+    }
+
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](lds_u8* base, int k0) {
+        const uint32_t b0 = (uint32_t)(uintptr_t)base + uwave * 1024;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) lds_dma16(a_src[i] + k0, b0 + i * 4096);
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * ldb, b0 + A_BYTES + i * 4096);
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wm = wave / WN, wn = wave % WN;
+
+    auto compute = [&](lds_u8* As) {
+        lds_u8* Bs = As + A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WTM + i * 16 + (l & 15);
+                const int c = (kk >> 3) + (l >> 4);
+                af[i] = *(lds_bf16x8*)(As + row * (BK * 2) + swz_a(row, c) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = wn * WTN + j * 16 + 4 * (l & 3);
+                const int c = n >> 3, half = (n >> 2) & 1;
+                s16x4 v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = kk + 8 * (l >> 4) + 4 * h + ((l & 15) >> 2);
+                    lds_u8* p = Bs + r * (BN * 2) + swz_b(r, c) * 16 + half * 8;
+                    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+                }
+                typedef __attribute__((ext_vector_type(8))) short s16x8;
+                const s16x8 both = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                bfr[j] = __builtin_bit_cast(bf16x8, both);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    const int nsteps = K / BK;  // >= 2 (checked on the host)
+    lds_u8* ring = (lds_u8*)smem;
+    issue(ring, 0);
+    issue(ring + Tl::STAGE, BK);
+    for (int s = 0; s < nsteps; ++s) {
+        // this step's loads have landed (the next step's may still fly) ...
+        if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::value);
+        else __builtin_amdgcn_s_waitcnt(VmWait<0>::value);
+        // ... in every wave, and every wave is done with step s-1's stage
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + 2 < nsteps) issue(ring + ((s + 2) % NS) * Tl::STAGE, (s + 2) * BK);
+        compute(ring + (s % NS) * Tl::STAGE);
+    }
+
+    // epilogue: lane holds rows 4*(l>>4)+q of column l&15 of every 16x16 tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + (l & 15);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = rb + wm * WTM + i * 16 + (l >> 4) * 4 + q;
+                if (row < re && col < N) {
+                    const float v = acc[i][j][q];
+                    if (EPI == 0)
+                        ((uint16_t*)C)[(long)row * ldc + col] = (uint16_t)f32_to_bf16_bits(silu_f32(v));
+                    else
+                        ((float*)C)[(long)row * ldc + col] = v;
+                }
+            }
+        }
+}
+
+}  // namespace dma
+}  // namespace moe

@@ -22,6 +22,7 @@
 // one register-prefetched stage in flight, 16x16x32 bf16 MFMA, fp32 acc.
 #include <math.h>
 
+#include "gemm_dma.hpp"
 #include "mfma_tiles.hpp"
 #include "moe_internal.hpp"
 
@@ -232,12 +233,33 @@ hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long l
     return hipGetLastError();
 }
 
+// Direct-to-LDS pipeline for large row counts (see gemm_dma.hpp).
+template <int BM, int BN, int EPI>
+hipError_t run_dma(const void* A, long lda, const void* B, long strideB, long ldb, void* C, long ldc,
+                   const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
+    const int n_tiles = (N + BN - 1) / BN;
+    // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
+    const long grid = max_mtiles(BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dma::gemm_dma_kernel<BM, BN, EPI>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const uint16_t*)A, lda, (const uint16_t*)B, strideB, ldb, C, ldc, offsets, E, fixed_rows, N, K,
+                       n_tiles);
+    return hipGetLastError();
+}
+
+inline bool dma_ok(long lda, long ldb, int N, int K) {
+    return K % 64 == 0 && K >= 128 && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
+}
+
 template <int EPI>
 hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, long strideB, long ldb, void* C,
                         long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K,
                         hipStream_t s) {
     switch (cfg) {
         case kTileM128:
+            if (dma_ok(lda, ldb, N, K))
+                return run_dma<128, 256, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows, max_rows, N,
+                                              K, s);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
         case kTileM64:
