@@ -145,8 +145,8 @@ def run_workload(name, steps, warmup, stage_reps):
     return I, res
 
 
-def cpu_baseline(I_name):
-    """The fp64 oracle, as it stands, on the host cores over the whole prefill batch."""
+def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
+    """The fp64 oracle, as it stands, on the host cores: whole prefill batches, repeated until about 10 s."""
     import numpy as np
 
     import gen
@@ -160,12 +160,17 @@ def cpu_baseline(I_name):
     I = gen.make_inputs(I_name)
     x, Wr = I.f64(I.x), I.f64(I.Wr)
     W1, W2 = I.f64(I.W1()), I.f64(I.W2())
-    t = time.perf_counter()
-    r = oracle.forward(x, Wr, I.bias_f64(), W1, W2, I.k, I.drop)
-    dt = time.perf_counter() - t
-    return {"value": round(I.T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole {I_name} batch (T={I.T}), fp64 numpy/OpenBLAS, {dt:.1f}s",
-            "stages_s": {k: round(v, 3) for k, v in r.times.items()}}
+    reps, total, stage = 0, 0.0, {}
+    while reps < max_reps and (total < min_seconds or reps == 0):
+        t = time.perf_counter()
+        r = oracle.forward(x, Wr, I.bias_f64(), W1, W2, I.k, I.drop)
+        total += time.perf_counter() - t
+        reps += 1
+        for k_, v in r.times.items():
+            stage[k_] = stage.get(k_, 0.0) + v
+    return {"value": round(reps * I.T / total, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} x the whole {I_name} batch (T={I.T} tokens), fp64 numpy/OpenBLAS, {total:.1f} s",
+            "stages_s": {k_: round(v / reps, 3) for k_, v in stage.items()}}
 
 
 def main():
@@ -176,6 +181,10 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one workload only (for profiling runs); prints its stage times")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run only a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -189,6 +198,19 @@ def main():
 
     moe.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return
+    if args.only:
+        _, res = run_workload(args.only, args.steps, args.warmup, args.stage_reps)
+        print(json.dumps({"workload": args.only, **res}), flush=True)
+        return
     I, pre = run_workload("prefill", args.steps, args.warmup, args.stage_reps)
     line = {
         "metric": "MoE-layer tokens/s + grouped-GEMM % MFMA peak, E=128 top-8 prefill & decode",
