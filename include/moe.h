@@ -79,11 +79,13 @@ const char* moe_version(void);
 
 /*
  * Bytes of device workspace that moe_forward needs for these sizes (Fs = 0:
- * no shared expert). It also covers moe_permute and moe_grouped_ffn, whose
- * own needs are moe_permute_workspace_bytes and moe_ffn_workspace_bytes.
+ * no shared expert). It also covers the step-wise calls, whose own needs are
+ * moe_route_workspace_bytes (0 when the router needs none),
+ * moe_permute_workspace_bytes and moe_ffn_workspace_bytes.
  * Returns 0 for sizes the library rejects. Host-only; no device access.
  */
 size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt);
+size_t moe_route_workspace_bytes(int T, int H, int E, moe_dtype_t dt);
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 size_t moe_ffn_workspace_bytes(int T, int F, int E, int k, int Fs, moe_dtype_t dt);
 
@@ -104,10 +106,14 @@ size_t moe_ffn_workspace_bytes(int T, int F, int E, int k, int Fs, moe_dtype_t d
  * x: [T,H] dt. Wr: [H,E] dt. bias: [E] fp32 or NULL (zero).
  * drop_thresh: 0 disables the drop; otherwise in (0, 1/k].
  * Out: topk_ids [T,k] int32, topk_w [T,k] fp32 (slot order: ascending id).
+ * ws: device workspace of moe_route_workspace_bytes(T,H,E,dt) bytes (fp32
+ * partial logits when the H loop is split across workgroups because T alone
+ * cannot fill the GPU; the partials are added in a fixed order, so results do
+ * not depend on timing). May be NULL when that size is 0.
  */
 int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
-              float drop_thresh, moe_dtype_t dt, int32_t* topk_ids, float* topk_w,
-              hipStream_t stream);
+              float drop_thresh, moe_dtype_t dt, int32_t* topk_ids, float* topk_w, void* ws,
+              size_t ws_bytes, hipStream_t stream);
 
 /*
  * moe_permute - dispatch: group the kept assignments by expert.

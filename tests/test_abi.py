@@ -65,12 +65,12 @@ def _p(v=0x1000):
 
 def test_route_rejects(lib):
     N = None
-    ok = dict(x=_p(), Wr=_p(), b=N, T=4, H=8, E=4, k=2, drop=0.0, dt=1, ids=_p(), w=_p(), s=N)
+    ok = dict(x=_p(), Wr=_p(), b=N, T=4, H=8, E=4, k=2, drop=0.0, dt=1, ids=_p(), w=_p(), ws=N, wsb=0, s=N)
 
     def call(**kw):
         a = dict(ok, **kw)
         return lib.moe_route(a["x"], a["Wr"], a["b"], a["T"], a["H"], a["E"], a["k"], a["drop"], a["dt"], a["ids"],
-                             a["w"], a["s"])
+                             a["w"], a["ws"], a["wsb"], a["s"])
 
     assert call(T=0) == moe.MOE_ERR_INVALID_ARG
     assert call(k=5) == moe.MOE_ERR_INVALID_ARG
@@ -83,6 +83,13 @@ def test_route_rejects(lib):
     assert call(dt=3) == moe.MOE_ERR_INVALID_ARG
     assert call(H=12) == moe.MOE_ERR_UNSUPPORTED
     assert call(E=2000, k=2) == moe.MOE_ERR_UNSUPPORTED
+    # a split router (few tokens, long H) needs its partial-logit workspace
+    need = lib.moe_route_workspace_bytes(32, 2048, 128, 1)
+    assert need == 32 * 32 * 128 * 4
+    assert call(T=32, H=2048, E=128, k=8) == moe.MOE_ERR_WORKSPACE
+    assert call(T=32, H=2048, E=128, k=8, ws=_p(), wsb=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route_workspace_bytes(8192, 2048, 128, 1) == 0   # enough token blocks: no split
+    assert lib.moe_route_workspace_bytes(32, 2048, 128, 0) == 0     # fp32 router never splits
 
 
 def test_permute_ffn_combine_forward_reject(lib):

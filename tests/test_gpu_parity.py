@@ -148,6 +148,26 @@ def test_small_layers(dev, name, over):
     assert torch.equal(y2, g["y"])
 
 
+@pytest.mark.parametrize("T,H,E,k,drop,zipf", [
+    (32, 512, 128, 8, 0.0, 0.0),      # few tokens: H loop split across workgroups, ordered reduction
+    (100, 256, 64, 4, 0.0, 0.0),
+    (3000, 128, 256, 8, 0.0, 0.0),    # one pass, E = 256
+    (50, 64, 16, 2, 0.0, 0.0),
+    (77, 192, 24, 3, 0.1, 1.2),       # E < 32 padded columns, bias, drop
+    (1, 1024, 40, 5, 0.0, 0.0),       # one token, many splits
+])
+def test_router_paths(dev, T, H, E, k, drop, zipf):
+    I = gen.make_inputs("tiny", T=T, H=H, F=64, E=E, k=k, dtype="bf16", seed=95 + T, drop=drop, zipf=zipf)
+    d = gen.to_device(I, dev)
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], I.k, I.drop)
+    ids2, w2 = moe.moe_route(d["x"], d["Wr"], d["bias"], I.k, I.drop)
+    torch.cuda.synchronize()
+    r = oracle.route(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.k, I.drop)
+    assert np.array_equal(ids.cpu().numpy(), r.ids)
+    assert np.abs(w.cpu().numpy() - r.w).max() <= W_TOL
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+
+
 def test_router_odd_expert_count(dev):
     """E % 8 != 0 takes the scalar Wr path of the bf16 router."""
     I = gen.make_inputs("tiny", T=70, H=64, F=64, E=13, k=3, dtype="bf16", seed=90)

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     moe_permute,
     moe_permute_workspace_bytes,
     moe_route,
+    moe_route_workspace_bytes,
     moe_workspace_bytes,
     strerror,
     version,

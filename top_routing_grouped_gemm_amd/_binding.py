@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_permute_workspace_bytes",
+EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_workspace_bytes",
+           "moe_permute_workspace_bytes",
            "moe_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward")
 
 
@@ -47,11 +48,13 @@ def load_library(path: Optional[str] = None):
     lib.moe_version.restype = ctypes.c_char_p
     lib.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.moe_workspace_bytes.restype = sz
+    lib.moe_route_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.moe_route_workspace_bytes.restype = sz
     lib.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
     lib.moe_permute_workspace_bytes.restype = sz
     lib.moe_ffn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.moe_ffn_workspace_bytes.restype = sz
-    lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp]
+    lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.moe_route.restype = i32
     lib.moe_permute.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i32
@@ -109,6 +112,11 @@ def moe_workspace_bytes(T, H, F, E, k, Fs=0, dtype=torch.bfloat16) -> int:
     return int(load_library().moe_workspace_bytes(T, H, F, E, k, Fs, dt))
 
 
+def moe_route_workspace_bytes(T, H, E, dtype=torch.bfloat16) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load_library().moe_route_workspace_bytes(T, H, E, dt))
+
+
 def moe_permute_workspace_bytes(T, E, k) -> int:
     return int(load_library().moe_permute_workspace_bytes(T, E, k))
 
@@ -122,15 +130,19 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def moe_route(x, Wr, bias, k: int, drop_thresh: float = 0.0, topk_ids=None, topk_w=None, stream=None):
+def moe_route(x, Wr, bias, k: int, drop_thresh: float = 0.0, topk_ids=None, topk_w=None, ws=None, stream=None):
     """Router logits, top-k, softmax weights (+ drop). Returns (topk_ids [T,k] int32, topk_w [T,k] fp32)."""
     T, H = x.shape
     E = Wr.shape[1]
     dev = x.device
     topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    need = moe_route_workspace_bytes(T, H, E, x.dtype)
+    if ws is None and need > 0:
+        ws = _ws(need, dev)
     st = load_library().moe_route(_ptr(x), _ptr(Wr), _ptr(bias), T, H, E, k, float(drop_thresh), _dt(x),
-                                  _ptr(topk_ids), _ptr(topk_w), _stream(stream))
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream))
     _check(st, "moe_route")
     return topk_ids, topk_w
 

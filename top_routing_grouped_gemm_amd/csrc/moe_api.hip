@@ -54,7 +54,7 @@ size_t permute_bytes(int T, int E, int k) {
 }
 
 struct FwdLayout {
-    size_t ids, w, offsets, inv, row_token, partial, x_perm, y_perm, y_sh, ffn, total;
+    size_t ids, w, offsets, inv, row_token, partial, x_perm, y_perm, y_sh, ffn, route, total;
 };
 
 FwdLayout fwd_layout(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) {
@@ -81,6 +81,8 @@ FwdLayout fwd_layout(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) 
     if (Fs > 0) off = align_up(off + (size_t)T * H * sizeof(float));
     L.ffn = off;
     off = align_up(off + ffn_layout(T, F, k, Fs, dt).total);
+    L.route = off;
+    off = align_up(off + moe::route_workspace_bytes(T, H, E, (Dtype)dt));
     L.total = off;
     return L;
 }
@@ -151,6 +153,11 @@ const char* moe_strerror(int status) {
 
 const char* moe_version(void) { return "0.1.0"; }
 
+size_t moe_route_workspace_bytes(int T, int H, int E, moe_dtype_t dt) {
+    if (!valid_dtype(dt) || check_sizes(T, H, 0, E, 1) != MOE_OK) return 0;
+    return moe::route_workspace_bytes(T, H, E, (Dtype)dt);
+}
+
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
     if (check_sizes(T, 8, 0, E, k) != MOE_OK) return 0;
     return permute_bytes(T, E, k);
@@ -167,13 +174,16 @@ size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs, moe_dtype_
 }
 
 int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k, float drop_thresh,
-              moe_dtype_t dt, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+              moe_dtype_t dt, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
     int st = check_sizes(T, H, 0, E, k);
     if (st != MOE_OK) return st;
     if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
     if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, topk_ids, topk_w, stream));
+    const size_t need = moe::route_workspace_bytes(T, H, E, (Dtype)dt);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    return hip_status(
+        moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, topk_ids, topk_w, ws, stream));
 }
 
 int moe_permute(const void* x, const int32_t* topk_ids, const float* topk_w, int T, int H, int E, int k,
@@ -242,8 +252,9 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
     float* y_perm = (float*)(base + L.y_perm);
     float* y_sh = fs > 0 ? (float*)(base + L.y_sh) : nullptr;
     void* ffn_ws = base + L.ffn;
+    void* route_ws = base + L.route;
 
-    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, stream));
+    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, route_ws, stream));
     if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, off, row_token, iv, partial, stream)) != MOE_OK)
         return st;
     if ((st = enqueue_ffn(x_perm, off, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_sh, ffn_ws, stream)) !=

@@ -17,8 +17,10 @@ enum TileCfg { kTileM16 = 0, kTileM64 = 1, kTileM128 = 2 };
 
 inline int dispatch_blocks(long n_assign) { return (int)((n_assign + kDispatchChunk - 1) / kDispatchChunk); }
 
+// Router workspace (fp32 partial logits when the H loop is split); 0 when none is needed.
+size_t route_workspace_bytes(int T, int H, int E, Dtype dt);
 hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
-                        float drop, Dtype dt, int32_t* ids, float* w, hipStream_t s);
+                        float drop, Dtype dt, int32_t* ids, float* w, void* ws, hipStream_t s);
 
 // Dispatch: per-chunk expert histograms -> scan -> stable ranks -> row copy.
 hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial,

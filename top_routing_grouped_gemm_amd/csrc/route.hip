@@ -15,6 +15,7 @@
 #include <float.h>
 #include <math.h>
 
+#include "gemm_dma.hpp"
 #include "mfma_tiles.hpp"
 #include "moe_internal.hpp"
 
@@ -243,6 +244,208 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined router (bf16, E % 8 == 0, E <= 256, H % 64 == 0): 32 tokens per
+// workgroup, the H loop streamed through a 3-stage direct-to-LDS ring (x rows
+// k-contiguous, Wr rows n-contiguous and read k-packed with LDS transpose
+// reads, as in the grouped GEMM). When the token blocks alone cannot fill the
+// GPU, the H loop is split across S workgroups that write fp32 partial logits;
+// a second kernel adds the S partials in a fixed order (reproducible) and runs
+// the top-k.
+constexpr int kR2Rows = 32;
+constexpr int kR2BK = 64;
+constexpr int kR2Stages = 3;
+
+template <int EP>
+struct R2 {
+    static constexpr int A_BYTES = kR2Rows * kR2BK * 2;      // 4 KiB: one chunk per wave
+    static constexpr int B_BYTES = kR2BK * EP * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int B_CHUNKS = B_BYTES / 4096;          // per wave
+    static constexpr int LOADS = 1 + B_CHUNKS;
+    static constexpr int B_RCH = EP / 8;                     // 16-byte chunks per Wr row
+    static constexpr int B_RPK = 1024 / (EP * 2);            // Wr rows per KiB
+    static constexpr int NT = EP / 16;                       // 16-column MFMA tiles
+    static constexpr int NTW = (NT + 3) / 4;                 // tiles per wave
+    static constexpr int LDS = (kR2Stages * STAGE > kR2Rows * EP * 4) ? kR2Stages * STAGE : kR2Rows * EP * 4;
+    static_assert(B_BYTES % 4096 == 0, "Wr tile must be whole 4 KiB chunks");
+    __device__ static int swz_b(int r, int c) { return EP >= 128 ? dma::swz_b(r, c) : c; }
+};
+
+template <int EP, bool SPLIT>
+__global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr,
+                                                       const float* __restrict__ bias, int T, int H, int E, int k,
+                                                       float drop, int steps_per_split, int32_t* __restrict__ ids,
+                                                       float* __restrict__ wout, float* __restrict__ partial) {
+    using C = R2<EP>;
+    __shared__ __align__(1024) uint8_t smem[C::LDS];
+    const int t0 = blockIdx.x * kR2Rows;
+    const int sp = blockIdx.y;
+    const int wave = threadIdx.x / kWave, l = lane_id();
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int kbase = sp * steps_per_split * kR2BK;
+
+    // global sources of this lane's LDS chunks
+    const int arow = 8 * uwave + (l >> 3);
+    const uint16_t* a_src = x + (long)min(t0 + arow, T - 1) * H + kbase + dma::swz_a(arow, l & 7) * 8;
+    const uint16_t* b_src[C::B_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < C::B_CHUNKS; ++i) {
+        const int c = uwave + 4 * i;
+        const int row = c * C::B_RPK + l / C::B_RCH;
+        const int col = min(C::swz_b(row, l % C::B_RCH) * 8, E - 8);
+        b_src[i] = Wr + (long)(kbase + row) * E + col;
+    }
+    dma::lds_u8* ring = (dma::lds_u8*)smem;
+    auto issue = [&](int stage, int k0) {
+        const uint32_t b0 = (uint32_t)(uintptr_t)(ring + stage * C::STAGE) + uwave * 1024;
+        dma::lds_dma16(a_src + k0, b0);
+#pragma unroll
+        for (int i = 0; i < C::B_CHUNKS; ++i) dma::lds_dma16(b_src[i] + (long)k0 * E, b0 + C::A_BYTES + i * 4096);
+    };
+
+    f32x4 acc[2][C::NTW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](dma::lds_u8* As) {
+        dma::lds_u8* Bs = As + C::A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < kR2BK; kk += 32) {
+            bf16x8 af[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = i * 16 + (l & 15);
+                af[i] = *(dma::lds_bf16x8*)(As + row * (kR2BK * 2) + dma::swz_a(row, (kk >> 3) + (l >> 4)) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < C::NTW; ++j) {
+                const int nt = wave + 4 * j;
+                if (nt < C::NT) {
+                    const int n = nt * 16 + 4 * (l & 3);
+                    const int c = n >> 3, half = (n >> 2) & 1;
+                    dma::s16x4 v[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int r = kk + 8 * (l >> 4) + 4 * h + ((l & 15) >> 2);
+                        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (dma::lds_s16x4*)(Bs + r * (EP * 2) + C::swz_b(r, c) * 16 + half * 8));
+                    }
+                    typedef __attribute__((ext_vector_type(8))) short s16x8;
+                    const bf16x8 bfr = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    const int nsteps = steps_per_split;
+    issue(0, 0);
+    if (nsteps > 1) issue(1, kR2BK);
+    for (int s = 0; s < nsteps; ++s) {
+        if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(dma::VmWait<C::LOADS>::value);
+        else __builtin_amdgcn_s_waitcnt(dma::VmWait<0>::value);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + 2 < nsteps) issue((s + 2) % kR2Stages, (s + 2) * kR2BK);
+        compute(ring + (s % kR2Stages) * C::STAGE);
+    }
+
+    if (SPLIT) {
+        // partial[sp][t][e], e over all EP columns (columns >= E are ignored later)
+#pragma unroll
+        for (int j = 0; j < C::NTW; ++j) {
+            const int nt = wave + 4 * j;
+            if (nt < C::NT) {
+                const int e = nt * 16 + (l & 15);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = t0 + i * 16 + (l >> 4) * 4 + q;
+                        if (t < T) partial[((long)sp * T + t) * EP + e] = acc[i][j][q];
+                    }
+            }
+        }
+        return;
+    }
+    asm volatile("" ::: "memory");
+    __syncthreads();  // all waves done with the ring before it holds logits
+    float* lg = (float*)smem;
+#pragma unroll
+    for (int j = 0; j < C::NTW; ++j) {
+        const int nt = wave + 4 * j;
+        if (nt < C::NT) {
+            const int e = nt * 16 + (l & 15);
+            const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) lg[(i * 16 + (l >> 4) * 4 + q) * EP + e] = acc[i][j][q] + b;
+        }
+    }
+    __syncthreads();
+    for (int m = wave; m < kR2Rows; m += 4) {
+        const long t = t0 + m;
+        if (t < T) topk_one_token(lg + m * EP, E, k, drop, t, ids, wout);
+    }
+}
+
+// Sum the S partial logits of each token in split order, add the bias, top-k.
+__global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restrict__ partial, int S, int T, int EP,
+                                                           const float* __restrict__ bias, int E, int k, float drop,
+                                                           int32_t* __restrict__ ids, float* __restrict__ wout) {
+    __shared__ float lg[4][256];
+    const int wave = threadIdx.x / kWave, l = lane_id();
+    const long t = (long)blockIdx.x * 4 + wave;
+    if (t >= T) return;  // wave-uniform; no barrier follows
+    for (int e = l; e < E; e += kWave) {
+        float v = 0.0f;
+        for (int s = 0; s < S; ++s) v += partial[((long)s * T + t) * EP + e];
+        lg[wave][e] = v + (bias != nullptr ? bias[e] : 0.0f);
+    }
+    topk_one_token(lg[wave], E, k, drop, t, ids, wout);
+}
+
+// Splits of the H loop: the smallest power of two that gives >= 256 workgroups
+// (and divides the number of 64-wide k-steps).
+inline int route_splits(int T, int H) {
+    const int blocks = (T + kR2Rows - 1) / kR2Rows;
+    const int steps = H / kR2BK;
+    int S = 1;
+    while (blocks * S < 256 && S * 2 <= steps && steps % (S * 2) == 0) S *= 2;
+    return S;
+}
+
+inline int route_ep(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256; }
+
+template <int EP>
+hipError_t launch_v2(const uint16_t* x, const uint16_t* Wr, const float* bias, int T, int H, int E, int k, float drop,
+                     int32_t* ids, float* w, float* partial, hipStream_t s) {
+    const int S = route_splits(T, H);
+    const int steps = H / kR2BK / S;
+    const dim3 grid((T + kR2Rows - 1) / kR2Rows, S);
+    if (S == 1) {
+        hipLaunchKernelGGL((route_v2_kernel<EP, false>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, k, drop, steps,
+                           ids, w, (float*)nullptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((route_v2_kernel<EP, true>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, k, drop, steps, ids,
+                       w, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_reduce_kernel, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)partial, S, T, EP, bias,
+                       E, k, drop, ids, w);
+    return hipGetLastError();
+}
+
+inline bool route_v2_ok(int H, int E) { return E % 8 == 0 && E <= 256 && H % kR2BK == 0; }
+
 template <int MT, int NTW>
 hipError_t launch_bf16(const uint16_t* x, const uint16_t* Wr, const float* bias, int T, int H, int E, int k,
                        float drop, int32_t* ids, float* w, hipStream_t s) {
@@ -263,11 +466,26 @@ hipError_t launch_bf16(const uint16_t* x, const uint16_t* Wr, const float* bias,
 
 }  // namespace
 
+size_t route_workspace_bytes(int T, int H, int E, Dtype dt) {
+    if (dt != kBF16 || !route_v2_ok(H, E)) return 0;
+    const int S = route_splits(T, H);
+    return S > 1 ? (size_t)S * T * route_ep(E) * sizeof(float) : 0;
+}
+
 hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k, float drop,
-                        Dtype dt, int32_t* ids, float* w, hipStream_t s) {
+                        Dtype dt, int32_t* ids, float* w, void* ws, hipStream_t s) {
     if (dt == kBF16) {
         const uint16_t* xb = (const uint16_t*)x;
         const uint16_t* wb = (const uint16_t*)Wr;
+        if (route_v2_ok(H, E)) {
+            float* part = (float*)ws;
+            switch (route_ep(E)) {
+                case 32: return launch_v2<32>(xb, wb, bias, T, H, E, k, drop, ids, w, part, s);
+                case 64: return launch_v2<64>(xb, wb, bias, T, H, E, k, drop, ids, w, part, s);
+                case 128: return launch_v2<128>(xb, wb, bias, T, H, E, k, drop, ids, w, part, s);
+                default: return launch_v2<256>(xb, wb, bias, T, H, E, k, drop, ids, w, part, s);
+            }
+        }
         const int ntiles = (E + 15) / 16;
         if (ntiles <= 8) return launch_bf16<2, 2>(xb, wb, bias, T, H, E, k, drop, ids, w, s);
         if (ntiles <= 16) return launch_bf16<2, 4>(xb, wb, bias, T, H, E, k, drop, ids, w, s);
