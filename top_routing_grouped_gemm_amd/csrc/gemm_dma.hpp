@@ -21,6 +21,9 @@
 // The loader applies the inverse permutation to the global addresses it
 // fetches, so every global row segment is still read contiguously.
 //
+// The router (route.hip) uses the same loader, swizzles and transpose reads
+// with 16x16x32 MFMAs; the grouped FFN uses gemm32_kernel below.
+//
 // Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin,
 // so workgroup b runs on XCD b % 8; the ragged tile sequence (experts in
 // order, M-tiles of an expert in order, N-tiles fastest) is cut into 8
@@ -34,6 +37,7 @@ namespace moe {
 namespace dma {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -111,152 +115,172 @@ __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, in
     return true;
 }
 
-// C[rows of group e, n-tile] = A[rows] @ B_e  with the fused epilogue.
-// Requirements (checked on the host): K % 64 == 0, K >= 128, N % 8 == 0, lda % 8 == 0,
-// ldb % 8 == 0.
+// C[rows of group e, n-tile] = A[rows] @ B_e with the fused epilogue, on
+// v_mfma_f32_32x32x16_bf16 (a single wave per SIMD sustains ~2 PFLOP/s with it,
+// against ~1.36 with the 16x16x32 form in the same loop).
+// Requirements (checked on the host): K % BK == 0, K >= 2*BK, N % 8 == 0,
+// lda % 8 == 0, ldb % 8 == 0.
 //
-// Pipeline: a ring of three LDS stages. k-step s waits (s_waitcnt vmcnt) for
-// its own loads, meets the other waves at a fence-free s_barrier (after which
-// every wave has landed step s and finished reading step s-1's stage),
-// starts the loads of step s+2 into that freed stage, then runs its MFMAs,
-// so two stages of loads are always in flight under the matrix work.
-template <int BM, int BN>
-struct DmaTile {
-    static constexpr int BK = 64;
-    static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BK * BN * 2;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+// Workgroup: WM x WN waves (8 by default: two per SIMD, which doubles the
+// number of direct-to-LDS loads in flight per CU; one wave's 16-byte loads
+// alone cap the L2-to-LDS feed near 12 TB/s chip-wide). Each wave owns a
+// (BM/WM) x (BN/WN) block of 32x32 accumulators.
+//
+// 32x32x16 operand and result lanes: A lane l holds row l%32, k-slice
+// 8*(l/32)..+7; B lane l holds column l%32 and the same k-slice, built from
+// two transpose reads (16-lane group G covers columns 16*(G&1)..+15 of the
+// tile and k-half G>>1); result lane l holds column l%32, rows
+// 8*(q/4) + 4*(l/32) + q%4 for q = 0..15.
+//
+// Pipeline: a ring of NS LDS stages of BK k-values. k-step s waits (s_waitcnt
+// vmcnt) for its own loads, meets the other waves at a fence-free s_barrier
+// (after which every wave has landed step s and finished reading the stage of
+// step s-1), starts the loads of step s+NS-1 into that freed stage, then runs
+// its MFMAs, so NS-1 stages of loads are always in flight.
+__device__ __forceinline__ int swz_b32(int r, int c) { return c ^ (4 * (r & 3)); }
+
+template <int BK>
+__device__ __forceinline__ int swz_a32(int r, int c) {
+    if constexpr (BK == 64) return c ^ ((r >> 1) & 7);  // 128-byte rows, 8 chunks
+    else return c ^ ((r >> 2) & 3);                     // 64-byte rows, 4 chunks
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN>
+struct Tile32 {
+    static constexpr int NW = WM * WN;
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_CHUNKS = A_BYTES / (1024 * NW), B_CHUNKS = B_BYTES / (1024 * NW);
+    static constexpr int LOADS = A_CHUNKS + B_CHUNKS;          // vm ops per lane per stage
+    static constexpr int A_RCH = BK / 8, A_RPK = 1024 / (BK * 2);
+    static constexpr int B_RCH = BN / 8, B_RPK = 1024 / (BN * 2);
+    static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+    static_assert(TM >= 1 && TN >= 1, "wave tile");
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole KiB chunks per wave");
+    static_assert(BN * 2 <= 1024 && BK * 2 <= 1024 && (BK == 32 || BK == 64), "row sizes");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t* __restrict__ A, long lda,
-                                                          const uint16_t* __restrict__ B, long strideB, long ldb,
-                                                          void* __restrict__ C, long ldc,
-                                                          const int32_t* __restrict__ offsets, int E, int fixed_rows,
-                                                          int N, int K, int n_tiles) {
-    using Tl = DmaTile<BM, BN>;
-    constexpr int BK = Tl::BK;
-    constexpr int A_BYTES = Tl::A_BYTES;
-    constexpr int B_BYTES = Tl::B_BYTES;
-    constexpr int A_CHUNKS = A_BYTES / 1024 / 4;   // 1 KiB chunks per wave
-    constexpr int B_CHUNKS = B_BYTES / 1024 / 4;
-    constexpr int LOADS = A_CHUNKS + B_CHUNKS;     // vm ops per thread per stage
-    constexpr int B_ROW_CHUNKS = BN / 8;           // 16-byte chunks per B row
-    constexpr int B_ROWS_PER_KB = 1024 / (BN * 2);
-    constexpr int WM = 2, WN = 2;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 16, TN = WTN / 16;
-    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile bytes");
-    static_assert(B_ROWS_PER_KB >= 1, "B row fits a KiB chunk");
-
-    constexpr int NS = 3;
-    __shared__ __align__(1024) uint8_t smem[NS * Tl::STAGE];
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t* __restrict__ A, long lda,
+                                                                 const uint16_t* __restrict__ B, long strideB,
+                                                                 long ldb, void* __restrict__ C, long ldc,
+                                                                 const int32_t* __restrict__ offsets, int E,
+                                                                 int fixed_rows, int N, int K, int n_tiles) {
+    using Tl = Tile32<BM, BN, BK, NS, WM, WN>;
+    constexpr int NW = Tl::NW, TM = Tl::TM, TN = Tl::TN, WTM = Tl::WTM, WTN = Tl::WTN;
+    constexpr int A_BYTES = Tl::A_BYTES, STAGE = Tl::STAGE, LOADS = Tl::LOADS;
+    __shared__ __align__(1024) uint8_t smem[NS * STAGE];
 
     int e, rb, re, nt;
     if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, e, rb, re, nt)) return;
     const int n0 = nt * BN;
     const uint16_t* Be = B + (long)e * strideB;
-
     const int wave = threadIdx.x / kWave, l = lane_id();
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
 
-    // --- per-lane global source of every LDS chunk this wave fills ---------
-    const uint16_t* a_src[A_CHUNKS];
+    // global source of each LDS chunk this lane fills (inverse XOR = same XOR)
+    const uint16_t* a_src[Tl::A_CHUNKS];
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-        const int c = wave + 4 * i;               // chunk: rows 8c .. 8c+7
-        const int row = 8 * c + (l >> 3);
-        const int pos = l & 7;
-        const int kc = swz_a(row, pos);           // the XOR is its own inverse
-        const int grow = min(rb + row, re - 1);   // rows past the group repeat a valid row
-        a_src[i] = A + (long)grow * lda + kc * 8;
+    for (int i = 0; i < Tl::A_CHUNKS; ++i) {
+        const int c = uwave + NW * i;
+        const int row = c * Tl::A_RPK + l / Tl::A_RCH;
+        const int grow = min(rb + row, re - 1);  // rows past the group repeat a valid row
+        a_src[i] = A + (long)grow * lda + swz_a32<BK>(row, l % Tl::A_RCH) * 8;
     }
-    const uint16_t* b_src[B_CHUNKS];
+    const uint16_t* b_src[Tl::B_CHUNKS];
 #pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-        const int c = wave + 4 * i;
-        const int row = c * B_ROWS_PER_KB + l / B_ROW_CHUNKS;
-        const int pos = l % B_ROW_CHUNKS;
-        const int cc = swz_b(row, pos);
-        const int col = min(n0 + cc * 8, N - 8);  // columns past N repeat a valid chunk
+    for (int i = 0; i < Tl::B_CHUNKS; ++i) {
+        const int c = uwave + NW * i;
+        const int row = c * Tl::B_RPK + l / Tl::B_RCH;
+        const int col = min(n0 + swz_b32(row, l % Tl::B_RCH) * 8, N - 8);  // columns past N repeat a valid chunk
         b_src[i] = Be + (long)row * ldb + col;
     }
-
-    const int uwave = __builtin_amdgcn_readfirstlane(wave);
-    auto issue = [&](lds_u8* base, int k0) {
-        const uint32_t b0 = (uint32_t)(uintptr_t)base + uwave * 1024;
+    lds_u8* ring = (lds_u8*)smem;
+    auto issue = [&](int stage, int k0) {
+        const uint32_t b0 = (uint32_t)(uintptr_t)(ring + stage * STAGE) + uwave * 1024;
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) lds_dma16(a_src[i] + k0, b0 + i * 4096);
+        for (int i = 0; i < Tl::A_CHUNKS; ++i) lds_dma16(a_src[i] + k0, b0 + i * 1024 * NW);
 #pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * ldb, b0 + A_BYTES + i * 4096);
+        for (int i = 0; i < Tl::B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * ldb, b0 + A_BYTES + i * 1024 * NW);
     };
 
-    f32x4 acc[TM][TN];
+    f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     const int wm = wave / WN, wn = wave % WN;
-
-    auto compute = [&](lds_u8* As) {
+    auto read_frags = [&](lds_u8* As, int ks, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
         lds_u8* Bs = As + A_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 af[TM], bfr[TN];
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (l & 31);
+            af[i] = *(lds_bf16x8*)(As + row * (BK * 2) + swz_a32<BK>(row, (ks >> 3) + (l >> 5)) * 16);
+        }
+        const int G = l >> 4, j4 = l & 15;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 16 + (l & 15);
-                const int c = (kk >> 3) + (l >> 4);
-                af[i] = *(lds_bf16x8*)(As + row * (BK * 2) + swz_a(row, c) * 16);
+        for (int j = 0; j < TN; ++j) {
+            const int n = wn * WTN + j * 32 + 16 * (G & 1) + 4 * (j4 & 3);
+            const int c = n >> 3, half = (n >> 2) & 1;
+            s16x4 v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = ks + 8 * (G >> 1) + 4 * h + (j4 >> 2);
+                v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(Bs + r * (BN * 2) + swz_b32(r, c) * 16 + half * 8));
             }
+            typedef __attribute__((ext_vector_type(8))) short s16x8;
+            bfr[j] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    auto mma = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = wn * WTN + j * 16 + 4 * (l & 3);
-                const int c = n >> 3, half = (n >> 2) & 1;
-                s16x4 v[2];
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int r = kk + 8 * (l >> 4) + 4 * h + ((l & 15) >> 2);
-                    lds_u8* p = Bs + r * (BN * 2) + swz_b(r, c) * 16 + half * 8;
-                    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-                }
-                typedef __attribute__((ext_vector_type(8))) short s16x8;
-                const s16x8 both = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                bfr[j] = __builtin_bit_cast(bf16x8, both);
-            }
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // fragments of the next 16-wide k-slice are read while the MFMAs of the current one run
+    auto compute = [&](lds_u8* As) {
+        bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+        read_frags(As, 0, a0, b0);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int ks = 0; ks < BK; ks += 32) {
+            read_frags(As, ks + 16, a1, b1);
+            mma(a0, b0);
+            if (ks + 32 < BK) read_frags(As, ks + 32, a0, b0);
+            mma(a1, b1);
         }
     };
 
-    const int nsteps = K / BK;  // >= 2 (checked on the host)
-    lds_u8* ring = (lds_u8*)smem;
-    issue(ring, 0);
-    issue(ring + Tl::STAGE, BK);
+    const int nsteps = K / BK;  // >= 2
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nsteps) issue(s, s * BK);
     for (int s = 0; s < nsteps; ++s) {
-        // this step's loads have landed (the next step's may still fly) ...
-        if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::value);
+        const int ahead = min(NS - 2, nsteps - 1 - s);  // stages after s already issued
+        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(VmWait<3 * LOADS>::value);
+        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(VmWait<2 * LOADS>::value);
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::value);
         else __builtin_amdgcn_s_waitcnt(VmWait<0>::value);
-        // ... in every wave, and every wave is done with step s-1's stage
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (s + 2 < nsteps) issue(ring + ((s + 2) % NS) * Tl::STAGE, (s + 2) * BK);
-        compute(ring + (s % NS) * Tl::STAGE);
+        if (s + NS - 1 < nsteps) issue((s + NS - 1) % NS, (s + NS - 1) * BK);
+        compute(ring + (s % NS) * STAGE);
     }
 
-    // epilogue: lane holds rows 4*(l>>4)+q of column l&15 of every 16x16 tile
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * 16 + (l & 15);
+            const int col = n0 + wn * WTN + j * 32 + (l & 31);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = rb + wm * WTM + i * 16 + (l >> 4) * 4 + q;
+            for (int q = 0; q < 16; ++q) {
+                const int row = rb + wm * WTM + i * 32 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
                 if (row < re && col < N) {
                     const float v = acc[i][j][q];
                     if (EPI == 0)

@@ -18,8 +18,10 @@
 // sized for the worst case (ceil(rows/BM) + min(E, rows) M-tiles) and
 // workgroups past the last tile exit at once.
 //
-// bf16 mainloop: 256 threads (4 waves), BM x BN x 64 tiles staged in LDS with
-// one register-prefetched stage in flight, 16x16x32 bf16 MFMA, fp32 acc.
+// Large row counts (>= 96 rows per expert on average) run the direct-to-LDS
+// pipeline of gemm_dma.hpp; smaller ones run the register-staged kernel below:
+// 256 threads (4 waves), BM x BN x 64 tiles staged in LDS with one prefetched
+// stage in flight, 16x16x32 bf16 MFMA, fp32 accumulation.
 #include <math.h>
 
 #include "gemm_dma.hpp"
@@ -233,22 +235,25 @@ hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long l
     return hipGetLastError();
 }
 
-// Direct-to-LDS pipeline for large row counts (see gemm_dma.hpp).
-template <int BM, int BN, int EPI>
+// Direct-to-LDS pipeline for large row counts (see gemm_dma.hpp): 256x256
+// tiles, 32-wide k-stages, a 4-stage ring, 8 waves.
+constexpr int kDmaBM = 256, kDmaBN = 256, kDmaBK = 32, kDmaNS = 4, kDmaWM = 4, kDmaWN = 2;
+
+template <int EPI>
 hipError_t run_dma(const void* A, long lda, const void* B, long strideB, long ldb, void* C, long ldc,
                    const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
-    const int n_tiles = (N + BN - 1) / BN;
+    const int n_tiles = (N + kDmaBN - 1) / kDmaBN;
     // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
-    const long grid = max_mtiles(BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
+    const long grid = max_mtiles(kDmaBM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dma::gemm_dma_kernel<BM, BN, EPI>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const uint16_t*)A, lda, (const uint16_t*)B, strideB, ldb, C, ldc, offsets, E, fixed_rows, N, K,
-                       n_tiles);
+    hipLaunchKernelGGL((dma::gemm32_kernel<kDmaBM, kDmaBN, kDmaBK, kDmaNS, kDmaWM, kDmaWN, EPI>), dim3((unsigned)grid),
+                       dim3(kDmaWM * kDmaWN * 64), 0, s, (const uint16_t*)A, lda, (const uint16_t*)B, strideB, ldb, C,
+                       ldc, offsets, E, fixed_rows, N, K, n_tiles);
     return hipGetLastError();
 }
 
 inline bool dma_ok(long lda, long ldb, int N, int K) {
-    return K % 64 == 0 && K >= 128 && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
+    return K % kDmaBK == 0 && K >= 2 * kDmaBK && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
 }
 
 template <int EPI>
@@ -258,8 +263,7 @@ hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, lon
     switch (cfg) {
         case kTileM128:
             if (dma_ok(lda, ldb, N, K))
-                return run_dma<128, 256, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows, max_rows, N,
-                                              K, s);
+                return run_dma<EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows, max_rows, N, K, s);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
         case kTileM64:
