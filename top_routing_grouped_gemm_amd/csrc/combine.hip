@@ -18,6 +18,8 @@ namespace moe {
 
 namespace {
 
+// Slots are processed 8 at a time with every load of a chunk issued before
+// any of its FMAs, so one thread keeps up to 8 row gathers in flight.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, const float4* __restrict__ ysh,
@@ -25,15 +27,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
     const long t = blockIdx.x;
     for (int c = threadIdx.x; c < H4; c += 256) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < k; ++j) {
-            const int r = inv[t * k + j];
-            if (r >= 0) {
-                const float ww = w[t * k + j];
-                const float4 v = y_perm[(long)r * H4 + c];
-                acc.x = fmaf(ww, v.x, acc.x);
-                acc.y = fmaf(ww, v.y, acc.y);
-                acc.z = fmaf(ww, v.z, acc.z);
-                acc.w = fmaf(ww, v.w, acc.w);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float4 v[8];
+            float ww[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                const int r = j < k ? inv[t * k + j] : -1;
+                ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
+                v[u] = r >= 0 ? y_perm[(long)r * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u < k && ww[u] != 0.0f) {  // slot order; dropped slots add nothing
+                    acc.x = fmaf(ww[u], v[u].x, acc.x);
+                    acc.y = fmaf(ww[u], v[u].y, acc.y);
+                    acc.z = fmaf(ww[u], v[u].z, acc.z);
+                    acc.w = fmaf(ww[u], v[u].w, acc.w);
+                }
             }
         }
         if (ysh != nullptr) {

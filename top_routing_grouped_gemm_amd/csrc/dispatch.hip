@@ -134,34 +134,37 @@ __global__ __launch_bounds__(kDispatchChunk) void index_kernel(const int32_t* __
     }
 }
 
-template <int U>
+// Each wave copies RPW consecutive destination rows: the source token of each
+// row is read once (wave-uniform), then every 16-byte load of all RPW rows is
+// issued before the stores.
+template <int RPW, int VPL>
 __global__ __launch_bounds__(256) void copy_rows_kernel(const u32x4* __restrict__ x,
                                                         const int32_t* __restrict__ row_token,
                                                         const int32_t* __restrict__ offsets, int E, int V,
-                                                        int rows_per_block, u32x4* __restrict__ out) {
+                                                        u32x4* __restrict__ out) {
     const int A = offsets[E];
-    const long r0 = (long)blockIdx.x * rows_per_block;
+    const int wave = threadIdx.x / kWave, l = lane_id();
+    const long r0 = ((long)blockIdx.x * 4 + wave) * RPW;
     if (r0 >= A) return;
-    const int nrows = (int)min((long)rows_per_block, (long)A - r0);
-    const int total = nrows * V;
-    for (int base = threadIdx.x; base < total; base += 256 * U) {
-        u32x4 v[U];
-        long dst[U];
+    long src[RPW];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = base + u * 256;
-            dst[u] = -1;
-            if (i < total) {
-                const long r = r0 + i / V;
-                const int c = i % V;
-                const long src = (long)row_token[r] * V + c;
-                v[u] = x[src];
-                dst[u] = r * V + c;
+    for (int i = 0; i < RPW; ++i) src[i] = (r0 + i < A) ? (long)row_token[r0 + i] * V : -1;
+    for (int c0 = 0; c0 < V; c0 += kWave * VPL) {
+        u32x4 v[RPW][VPL];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int c = c0 + u * kWave + l;
+                if (src[i] >= 0 && c < V) v[i][u] = x[src[i] + c];
             }
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (dst[u] >= 0) out[dst[u]] = v[u];
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int c = c0 + u * kWave + l;
+                if (src[i] >= 0 && c < V) out[(r0 + i) * V + c] = v[i][u];
+            }
     }
 }
 
@@ -191,13 +194,12 @@ hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* parti
 hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
                             int row_bytes, void* x_perm, hipStream_t s) {
     const int V = row_bytes / 16;
-    constexpr int U = 8;
-    int rpb = (256 * U) / V;
-    if (rpb < 1) rpb = 1;
-    const int grid = (max_rows + rpb - 1) / rpb;
+    constexpr int RPW = 4, VPL = 4;  // 16 loads of 16 bytes in flight per lane
+    const long rows_per_block = 4L * RPW;
+    const long grid = (max_rows + rows_per_block - 1) / rows_per_block;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((copy_rows_kernel<U>), dim3(grid), dim3(256), 0, s, (const u32x4*)x, row_token, offsets, E,
-                       V, rpb, (u32x4*)x_perm);
+    hipLaunchKernelGGL((copy_rows_kernel<RPW, VPL>), dim3((unsigned)grid), dim3(256), 0, s, (const u32x4*)x, row_token,
+                       offsets, E, V, (u32x4*)x_perm);
     return hipGetLastError();
 }
 

@@ -412,13 +412,14 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restri
     topk_one_token(lg[wave], E, k, drop, t, ids, wout);
 }
 
-// Splits of the H loop: the smallest power of two that gives >= 256 workgroups
-// (and divides the number of 64-wide k-steps).
+// Splits of the H loop: the smallest power of two that gives >= 1024
+// workgroups (about four per CU, for enough loads in flight) and divides the
+// number of 64-wide k-steps.
 inline int route_splits(int T, int H) {
     const int blocks = (T + kR2Rows - 1) / kR2Rows;
     const int steps = H / kR2BK;
     int S = 1;
-    while (blocks * S < 256 && S * 2 <= steps && steps % (S * 2) == 0) S *= 2;
+    while (blocks * S < 1024 && S * 2 <= steps && steps % (S * 2) == 0) S *= 2;
     return S;
 }
 
