@@ -240,15 +240,15 @@ hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long l
 constexpr int kDmaBM = 256, kDmaBN = 256, kDmaBK = 32, kDmaNS = 4, kDmaWM = 4, kDmaWN = 2;
 
 template <int EPI>
-hipError_t run_dma(const void* A, long lda, const void* B, long strideB, long ldb, void* C, long ldc,
-                   const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
+hipError_t run_dma(const void* A, long lda, const int32_t* a_rows, const void* B, long strideB, long ldb, void* C,
+                   long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
     const int n_tiles = (N + kDmaBN - 1) / kDmaBN;
     // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
     const long grid = max_mtiles(kDmaBM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm32_kernel<kDmaBM, kDmaBN, kDmaBK, kDmaNS, kDmaWM, kDmaWN, EPI>), dim3((unsigned)grid),
-                       dim3(kDmaWM * kDmaWN * 64), 0, s, (const uint16_t*)A, lda, (const uint16_t*)B, strideB, ldb, C,
-                       ldc, offsets, E, fixed_rows, N, K, n_tiles);
+                       dim3(kDmaWM * kDmaWN * 64), 0, s, (const uint16_t*)A, lda, a_rows, (const uint16_t*)B, strideB,
+                       ldb, C, ldc, offsets, E, fixed_rows, N, K, n_tiles);
     return hipGetLastError();
 }
 
@@ -263,7 +263,8 @@ hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, lon
     switch (cfg) {
         case kTileM128:
             if (dma_ok(lda, ldb, N, K))
-                return run_dma<EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows, max_rows, N, K, s);
+                return run_dma<EPI>(A, lda, nullptr, B, strideB, ldb, C, ldc, offsets, E, fixed_rows, max_rows, N, K,
+                                    s);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
         case kTileM64:
@@ -288,6 +289,15 @@ hipError_t run_f32(const void* A, long lda, const void* B, long strideB, long ld
 }
 
 }  // namespace
+
+bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt) {
+    return dt == kBF16 && cfg == kTileM128 && dma_ok(H, F, F, H);
+}
+
+hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
+                                const void* W1, int H, int F, void* h, hipStream_t s) {
+    return run_dma<kEpiSiluOut>(x, H, row_token, W1, (long)H * F, F, h, F, offsets, E, 0, max_rows, F, H, s);
+}
 
 TileCfg choose_tile(long rows, int groups) {
     const long mean = groups > 0 ? rows / groups : rows;

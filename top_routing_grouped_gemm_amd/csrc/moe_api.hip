@@ -95,27 +95,33 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
         if (_e != hipSuccess) return MOE_ERR_HIP; \
     } while (0)
 
+// copy_rows = false: only the routing maps (offsets, row_token, inv) are
+// built and x_perm is left unwritten (the W1 launch then gathers x rows).
 int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, int H, int E, int k,
                     moe_dtype_t dt, void* x_perm, int32_t* offsets, int32_t* row_token, int32_t* inv,
-                    int32_t* partial, hipStream_t s) {
+                    int32_t* partial, bool copy_rows, hipStream_t s) {
     const int n = T * k;
     MOE_TRY(moe::launch_count(ids, w, n, E, partial, s));
     MOE_TRY(moe::launch_scan(partial, moe::dispatch_blocks(n), E, offsets, s));
     MOE_TRY(moe::launch_index(ids, w, partial, n, k, E, row_token, inv, s));
-    MOE_TRY(moe::launch_copy_rows(x, row_token, offsets, E, n, (int)(H * elem_bytes(dt)), x_perm, s));
+    if (copy_rows) MOE_TRY(moe::launch_copy_rows(x, row_token, offsets, E, n, (int)(H * elem_bytes(dt)), x_perm, s));
     return MOE_OK;
 }
 
-int enqueue_ffn(const void* x_perm, const int32_t* offsets, const void* W1, const void* W2, int T, int H, int F,
-                int E, int k, moe_dtype_t dt, float* y_perm, const void* x, const void* W1s, const void* W2s,
-                int Fs, float* y_shared, void* ws, hipStream_t s) {
+// row_token != NULL: the W1 launch gathers rows of x through row_token instead of reading x_perm.
+int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* offsets, const void* W1, const void* W2,
+                int T, int H, int F, int E, int k, moe_dtype_t dt, float* y_perm, const void* x, const void* W1s,
+                const void* W2s, int Fs, float* y_shared, void* ws, hipStream_t s) {
     const FfnLayout L = ffn_layout(T, F, k, Fs, dt);
     char* base = (char*)ws;
     void* h = base + L.h;
     const Dtype d = (Dtype)dt;
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
-    MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, s));
+    if (row_token != nullptr)
+        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, h, s));
+    else
+        MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, s));
     if (W1s != nullptr) {
         void* hs = base + L.h_sh;
         const moe::TileCfg cs = moe::choose_tile(T, 1);
@@ -196,7 +202,7 @@ int moe_permute(const void* x, const int32_t* topk_ids, const float* topk_w, int
         return MOE_ERR_INVALID_ARG;
     if (ws_bytes < permute_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
     return enqueue_permute(x, topk_ids, topk_w, T, H, E, k, dt, x_perm, expert_offsets, row_token, inv,
-                           (int32_t*)ws, stream);
+                           (int32_t*)ws, true, stream);
 }
 
 int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const void* W1, const void* W2, int T, int H,
@@ -210,8 +216,8 @@ int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const voi
     if (!x_perm || !expert_offsets || !W1 || !W2 || !y_perm || !ws) return MOE_ERR_INVALID_ARG;
     const int fs = W1s ? Fs : 0;
     if (ws_bytes < ffn_layout(T, F, k, fs, dt).total) return MOE_ERR_WORKSPACE;
-    return enqueue_ffn(x_perm, expert_offsets, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_shared, ws,
-                       stream);
+    return enqueue_ffn(x_perm, nullptr, expert_offsets, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_shared,
+                       ws, stream);
 }
 
 int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, const float* y_shared, int T, int H,
@@ -254,11 +260,14 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
     void* ffn_ws = base + L.ffn;
     void* route_ws = base + L.route;
 
+    // large row counts: the W1 launch gathers x rows itself and x_perm is never written
+    const bool gather = moe::ffn_up_gathers(moe::choose_tile((long)T * k, E), H, F, (Dtype)dt);
     MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, route_ws, stream));
-    if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, off, row_token, iv, partial, stream)) != MOE_OK)
-        return st;
-    if ((st = enqueue_ffn(x_perm, off, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_sh, ffn_ws, stream)) !=
+    if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, off, row_token, iv, partial, !gather, stream)) !=
         MOE_OK)
+        return st;
+    if ((st = enqueue_ffn(x_perm, gather ? row_token : nullptr, off, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs,
+                          y_sh, ffn_ws, stream)) != MOE_OK)
         return st;
     return hip_status(moe::launch_combine(y_perm, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
 }

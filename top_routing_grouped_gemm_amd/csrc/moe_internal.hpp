@@ -38,6 +38,11 @@ hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed
 hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
                            const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, hipStream_t s);
 TileCfg choose_tile(long rows, int groups);
+// Whether the W1 launch for this tile shape can read token rows of x directly
+// through the row -> token map (the permute copy is then not needed).
+bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt);
+hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
+                                const void* W1, int H, int F, void* h, hipStream_t s);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared,
                           int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
