@@ -50,6 +50,11 @@ template <int N>
 struct VmWait {
     static constexpr int value = (N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14);
 };
+// vmcnt <= n and lgkmcnt == 0 (every LDS read of this wave has returned).
+template <int N>
+struct VmLgkmWait {
+    static constexpr int value = (N & 15) | (7 << 4) | (((N >> 4) & 3) << 14);
+};
 
 // One direct-to-LDS 16-byte load per lane: lane i's 16 bytes from `src` land
 // at LDS byte address lds_base + 16 * i (lds_base wave-uniform, via M0).
@@ -145,7 +150,7 @@ __device__ __forceinline__ int swz_a32(int r, int c) {
     else return c ^ ((r >> 2) & 3);                     // 64-byte rows, 4 chunks
 }
 
-// Epilogue helpers shared by the 32x32 kernels.
+// Epilogue helpers of the 32x32 kernel.
 __device__ __forceinline__ float dpp_swap1(float v) {  // lane i <- lane i^1 within quads
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
@@ -283,7 +288,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = uwave / WN, wn = uwave % WN;
+    // A wave whose 64 rows all lie past the group's end (the ragged last M-tile
+    // of a group) skips its LDS reads, MFMAs and stores but keeps its share of
+    // the loads and barriers. Waves w and w+4 share a SIMD and cover opposite
+    // row halves, so a tile with <= BM/2 valid rows runs in about half the time.
+    const bool active = rb + wm * WTM < re;
     auto read_frags = [&](lds_u8* As, int ks, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
         lds_u8* Bs = As + A_BYTES;
 #pragma unroll
@@ -314,18 +324,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
-    // fragments of the next 16-wide k-slice are read while the MFMAs of the current one run
-    auto compute = [&](lds_u8* As) {
-        bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-        read_frags(As, 0, a0, b0);
-#pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            read_frags(As, ks + 16, a1, b1);
-            mma(a0, b0);
-            if (ks + 32 < BK) read_frags(As, ks + 32, a0, b0);
-            mma(a1, b1);
-        }
-    };
+    // Fragments of k-slice j are read while the MFMAs of slice j-1 run. The
+    // last slice of a stage is multiplied only after the next barrier, so the
+    // MFMA pipe still has work while the first reads of the new stage are in
+    // flight; its reads must have landed before the barrier (lgkmcnt(0)) since
+    // the barrier releases that stage to the next loads.
+    constexpr int KS = BK / 16;
+    static_assert(KS % 2 == 0, "the deferred slice lives in fragment buffer 1");
+    bf16x8 fa[2][TM], fb[2][TN];
 
     const int nsteps = K / BK;  // >= 2
 #pragma unroll
@@ -333,238 +339,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
         if (s < nsteps) issue(s, s * BK);
     for (int s = 0; s < nsteps; ++s) {
         const int ahead = min(NS - 2, nsteps - 1 - s);  // stages after s already issued
-        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(VmWait<3 * LOADS>::value);
-        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(VmWait<2 * LOADS>::value);
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::value);
-        else __builtin_amdgcn_s_waitcnt(VmWait<0>::value);
+        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(VmLgkmWait<3 * LOADS>::value);
+        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(VmLgkmWait<2 * LOADS>::value);
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VmLgkmWait<LOADS>::value);
+        else __builtin_amdgcn_s_waitcnt(VmLgkmWait<0>::value);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (s + NS - 1 < nsteps) issue((s + NS - 1) % NS, (s + NS - 1) * BK);
-        compute(ring + (s % NS) * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) {
+            lds_u8* As = ring + (s % NS) * STAGE;
+            read_frags(As, 0, fa[0], fb[0]);
+            if (s > 0) mma(fa[1], fb[1]);
+#pragma unroll
+            for (int j = 1; j < KS; ++j) {
+                read_frags(As, 16 * j, fa[j & 1], fb[j & 1]);
+                mma(fa[(j - 1) & 1], fb[(j - 1) & 1]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (!active) return;
+    mma(fa[1], fb[1]);
 
     store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, rb, re, n0, N, wm, wn);
-}
-
-// ---------------------------------------------------------------------------
-// Persistent variant: one workgroup per CU walks its share of the XCD's tile
-// chunk (tiles x*chunk + q, + q + Q, ... for workgroup q of the Q on XCD x).
-// The LDS ring runs across tile boundaries, so the next tile's first stages
-// load while the current tile's epilogue runs. The per-group row offsets and
-// the ragged tile prefix are read once into LDS.
-//
-// Epilogue: a quad transpose (two DPP exchanges) gives each lane 4 adjacent
-// columns of one output row, written with one 16-byte (fp32) or 8-byte (bf16)
-// buffer store; rows past the group and columns past N get an out-of-range
-// offset and are dropped by the buffer descriptor, so no store sits behind a
-// branch.
-//
-// Waits: the kernel counts the loads it issues and, before reading a stage,
-// waits until no more than the loads issued after that stage are outstanding.
-// Loads complete in issue order, so this holds whatever order the epilogue's
-// stores complete in (a pending store can only make the wait longer).
-constexpr int kMaxGroups = 1024;
-
-__device__ __forceinline__ void wait_vm_dynamic(int n) {
-    // s_waitcnt needs an immediate: binary tree over 0..63 (n >= 63 -> 63, stricter)
-#define MOE_W(k) case k: __builtin_amdgcn_s_waitcnt(VmWait<k>::value); break;
-    switch (n < 63 ? n : 63) {
-        MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7) MOE_W(8) MOE_W(9) MOE_W(10)
-        MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15) MOE_W(16) MOE_W(17) MOE_W(18) MOE_W(19) MOE_W(20)
-        MOE_W(21) MOE_W(22) MOE_W(23) MOE_W(24) MOE_W(25) MOE_W(26) MOE_W(27) MOE_W(28) MOE_W(29) MOE_W(30)
-        MOE_W(31) MOE_W(32) MOE_W(33) MOE_W(34) MOE_W(35) MOE_W(36) MOE_W(37) MOE_W(38) MOE_W(39) MOE_W(40)
-        MOE_W(41) MOE_W(42) MOE_W(43) MOE_W(44) MOE_W(45) MOE_W(46) MOE_W(47) MOE_W(48) MOE_W(49) MOE_W(50)
-        MOE_W(51) MOE_W(52) MOE_W(53) MOE_W(54) MOE_W(55) MOE_W(56) MOE_W(57) MOE_W(58) MOE_W(59) MOE_W(60)
-        MOE_W(61) MOE_W(62) default: __builtin_amdgcn_s_waitcnt(VmWait<63>::value); break;
-    }
-#undef MOE_W
-}
-
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm32p_kernel(const uint16_t* __restrict__ A, long lda,
-                                                                  const uint16_t* __restrict__ B, long strideB,
-                                                                  long ldb, void* __restrict__ C, long ldc,
-                                                                  const int32_t* __restrict__ offsets, int E,
-                                                                  int fixed_rows, int N, int K, int n_tiles) {
-    using Tl = Tile32<BM, BN, BK, NS, WM, WN>;
-    constexpr int NW = Tl::NW, TM = Tl::TM, TN = Tl::TN, WTM = Tl::WTM, WTN = Tl::WTN;
-    constexpr int A_BYTES = Tl::A_BYTES, STAGE = Tl::STAGE, LOADS = Tl::LOADS;
-    __shared__ __align__(1024) uint8_t smem[NS * STAGE];
-    __shared__ int s_off[kMaxGroups + 1];
-    __shared__ int s_tile[kMaxGroups + 1];
-
-    const int wave = threadIdx.x / kWave, l = lane_id();
-    const int uwave = __builtin_amdgcn_readfirstlane(wave);
-    const int G = offsets != nullptr ? E : 1;
-    for (int i = threadIdx.x; i <= G; i += NW * kWave)
-        s_off[i] = offsets != nullptr ? offsets[i] : (i == 0 ? 0 : fixed_rows);
-    __syncthreads();
-    if (wave == 0) {  // s_tile[g] = M-tiles of the groups before g
-        const int per = (G + kWave - 1) / kWave;
-        const int g0 = min(G, l * per), g1 = min(G, g0 + per);
-        int s = 0;
-        for (int g = g0; g < g1; ++g) s += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
-        const int incl = wave_incl_scan(s);
-        int run = incl - s;
-        for (int g = g0; g < g1; ++g) {
-            s_tile[g] = run;
-            run += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
-        }
-        if (l == kWave - 1) s_tile[G] = incl;
-    }
-    __syncthreads();
-    const long total = (long)s_tile[G] * n_tiles;
-    const long chunk = (total + kXcds - 1) / kXcds;
-    const int nq = gridDim.x / kXcds;
-    const long t_begin = (long)(blockIdx.x % kXcds) * chunk + blockIdx.x / kXcds;
-    const long t_end = min((long)(blockIdx.x % kXcds + 1) * chunk, total);
-    const int my_tiles = t_begin < t_end ? (int)((t_end - t_begin + nq - 1) / nq) : 0;
-    if (my_tiles == 0) return;
-    const int nsteps = K / BK;
-    const int total_steps = my_tiles * nsteps;
-
-    // tile j of this workgroup -> group, row range, first column
-    auto decode = [&](int j, int& g, int& rb, int& re, int& n0) {
-        const long t = t_begin + (long)j * nq;
-        const int mt = (int)(t / n_tiles);
-        n0 = (int)(t % n_tiles) * BN;
-        int lo = 0, hi = G;  // last g with s_tile[g] <= mt (skips empty groups)
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_tile[mid] <= mt) lo = mid;
-            else hi = mid;
-        }
-        g = lo;
-        rb = s_off[g] + (mt - s_tile[g]) * BM;
-        re = min(s_off[g + 1], rb + BM);
-    };
-
-    // ---- issue side: global sources of the tile being loaded -----------------
-    const uint16_t* a_src[Tl::A_CHUNKS];
-    const uint16_t* b_src[Tl::B_CHUNKS];
-    auto setup_issue = [&](int j) {
-        int g, rb, re, n0;
-        decode(j, g, rb, re, n0);
-        const uint16_t* Bg = B + (long)g * strideB;
-#pragma unroll
-        for (int i = 0; i < Tl::A_CHUNKS; ++i) {
-            const int c = uwave + NW * i;
-            const int row = c * Tl::A_RPK + l / Tl::A_RCH;
-            a_src[i] = A + (long)min(rb + row, re - 1) * lda + swz_a32<BK>(row, l % Tl::A_RCH) * 8;
-        }
-#pragma unroll
-        for (int i = 0; i < Tl::B_CHUNKS; ++i) {
-            const int c = uwave + NW * i;
-            const int row = c * Tl::B_RPK + l / Tl::B_RCH;
-            b_src[i] = Bg + (long)row * ldb + min(n0 + swz_b32(row, l % Tl::B_RCH) * 8, N - 8);
-        }
-    };
-    lds_u8* ring = (lds_u8*)smem;
-    int issued = 0;       // loads issued so far by this lane (wave-uniform)
-    int mark[NS];         // `issued` right after each slot's loads
-    int it_j = 0, it_s = 0;
-    auto issue_next = [&](int slot) {
-        const uint32_t b0 = (uint32_t)(uintptr_t)(ring + slot * STAGE) + uwave * 1024;
-        const int k0 = it_s * BK;
-#pragma unroll
-        for (int i = 0; i < Tl::A_CHUNKS; ++i) lds_dma16(a_src[i] + k0, b0 + i * 1024 * NW);
-#pragma unroll
-        for (int i = 0; i < Tl::B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * ldb, b0 + A_BYTES + i * 1024 * NW);
-        issued += LOADS;
-#pragma unroll
-        for (int q = 0; q < NS; ++q)
-            if (q == slot) mark[q] = issued;
-        if (++it_s == nsteps) {
-            it_s = 0;
-            if (++it_j < my_tiles) setup_issue(it_j);
-        }
-    };
-
-    // ---- compute side ----------------------------------------------------------
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-    const int wm = wave / WN, wn = wave % WN;
-    auto read_frags = [&](lds_u8* As, int ks, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
-        lds_u8* Bs = As + A_BYTES;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm * WTM + i * 32 + (l & 31);
-            af[i] = *(lds_bf16x8*)(As + row * (BK * 2) + swz_a32<BK>(row, (ks >> 3) + (l >> 5)) * 16);
-        }
-        const int Gq = l >> 4, j4 = l & 15;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = wn * WTN + j * 32 + 16 * (Gq & 1) + 4 * (j4 & 3);
-            const int c = n >> 3, half = (n >> 2) & 1;
-            s16x4 v[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int r = ks + 8 * (Gq >> 1) + 4 * h + (j4 >> 2);
-                v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(Bs + r * (BN * 2) + swz_b32(r, c) * 16 + half * 8));
-            }
-            typedef __attribute__((ext_vector_type(8))) short s16x8;
-            bfr[j] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    };
-    auto mma = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    };
-    auto compute = [&](lds_u8* As) {
-        bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-        read_frags(As, 0, a0, b0);
-#pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            read_frags(As, ks + 16, a1, b1);
-            mma(a0, b0);
-            if (ks + 32 < BK) read_frags(As, ks + 32, a0, b0);
-            mma(a1, b1);
-        }
-    };
-    auto epilogue = [&](int j) {
-        int g, rb, re, n0;
-        decode(j, g, rb, re, n0);
-        store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, rb, re, n0, N, wm, wn);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x16{};
-    };
-
-    setup_issue(0);
-#pragma unroll
-    for (int q = 0; q < NS - 1; ++q)
-        if (q < total_steps) issue_next(q);
-    int cj = 0, cs = 0;
-    for (int gs = 0; gs < total_steps; ++gs) {
-        const int slot = gs % NS;
-        int mk = 0;
-#pragma unroll
-        for (int q = 0; q < NS; ++q)
-            if (q == slot) mk = mark[q];
-        wait_vm_dynamic(issued - mk);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (gs + NS - 1 < total_steps) issue_next((gs + NS - 1) % NS);
-        compute(ring + slot * STAGE);
-        if (++cs == nsteps) {
-            epilogue(cj);
-            cs = 0;
-            ++cj;
-        }
-    }
 }
 
 }  // namespace dma

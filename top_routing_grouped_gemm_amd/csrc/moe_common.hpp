@@ -48,6 +48,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
-__device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + __expf(-u)); }
+// SiLU(u) = u * sigmoid(u) = u / (1 + e^-u), with the hardware reciprocal
+// (about 1 ulp) in place of an IEEE divide: the value is rounded to bf16 or
+// fed to an fp32 contraction next, so the last bit does not matter, and the
+// divide sequence would cost the GEMM epilogue ~10 VALU ops per element.
+// Large negative u: e^-u = inf, rcp(inf) = 0, result -0.
+__device__ __forceinline__ float silu_f32(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
 
 }  // namespace moe
