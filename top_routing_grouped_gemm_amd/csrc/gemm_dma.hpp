@@ -56,6 +56,20 @@ struct VmLgkmWait {
     static constexpr int value = (N & 15) | (7 << 4) | (((N >> 4) & 3) << 14);
 };
 
+// Wait until at most `ahead` later stages of LOADS loads each are still in
+// flight (loads complete in issue order), with all LDS reads returned.
+// s_waitcnt takes an immediate, hence the unrolled ladder over ahead = MAXA..0.
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_stage(int ahead) {
+    static_assert(MAXA * LOADS <= 63, "vmcnt is 6 bits");
+    if constexpr (MAXA == 0) {
+        __builtin_amdgcn_s_waitcnt(VmLgkmWait<0>::value);
+    } else {
+        if (ahead >= MAXA) __builtin_amdgcn_s_waitcnt(VmLgkmWait<MAXA * LOADS>::value);
+        else wait_stage<LOADS, MAXA - 1>(ahead);
+    }
+}
+
 // One direct-to-LDS 16-byte load per lane: lane i's 16 bytes from `src` land
 // at LDS byte address lds_base + 16 * i (lds_base wave-uniform, via M0).
 // Issued from inline asm so that the compiler does not track it as an LDS
@@ -338,11 +352,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     for (int s = 0; s < NS - 1; ++s)
         if (s < nsteps) issue(s, s * BK);
     for (int s = 0; s < nsteps; ++s) {
-        const int ahead = min(NS - 2, nsteps - 1 - s);  // stages after s already issued
-        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(VmLgkmWait<3 * LOADS>::value);
-        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(VmLgkmWait<2 * LOADS>::value);
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VmLgkmWait<LOADS>::value);
-        else __builtin_amdgcn_s_waitcnt(VmLgkmWait<0>::value);
+        wait_stage<LOADS, NS - 2>(min(NS - 2, nsteps - 1 - s));  // stages after s already issued
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");

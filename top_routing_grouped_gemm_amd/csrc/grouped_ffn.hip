@@ -235,25 +235,36 @@ hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long l
     return hipGetLastError();
 }
 
-// Direct-to-LDS pipeline for large row counts (see gemm_dma.hpp): 256x256
-// tiles, 32-wide k-stages, a 4-stage ring, 8 waves.
-constexpr int kDmaBM = 256, kDmaBN = 256, kDmaBK = 32, kDmaNS = 4, kDmaWM = 4, kDmaWN = 2;
+// Direct-to-LDS pipelines (gemm_dma.hpp), one shape per regime:
+//  - DmaLarge: many rows per group (prefill). 256x256 tiles, 32-wide
+//    k-stages, a 4-stage ring, 8 waves; MFMA-bound when fed.
+//  - DmaStream: a few rows per group (decode). Each tile is one 32-row MFMA
+//    block against a 128-column weight slab; 64-wide k-stages in a 6-stage
+//    ring keep ~100 KB of weight loads in flight per CU, which is what
+//    streaming the expert weights at HBM rate needs.
+template <int BM_, int BN_, int BK_, int NS_, int WM_, int WN_>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
+};
+using DmaLarge = DmaCfg<256, 256, 32, 4, 4, 2>;
+using DmaStream = DmaCfg<32, 128, 64, 6, 1, 4>;
 
-template <int EPI>
-hipError_t run_dma(const void* A, long lda, const int32_t* a_rows, const void* B, long strideB, long ldb, void* C,
+template <class C, int EPI>
+hipError_t run_dma(const void* A, long lda, const int32_t* a_rows, const void* B, long strideB, long ldb, void* Cm,
                    long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
-    const int n_tiles = (N + kDmaBN - 1) / kDmaBN;
+    const int n_tiles = (N + C::BN - 1) / C::BN;
     // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
-    const long grid = max_mtiles(kDmaBM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
+    const long grid = max_mtiles(C::BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dma::gemm32_kernel<kDmaBM, kDmaBN, kDmaBK, kDmaNS, kDmaWM, kDmaWN, EPI>), dim3((unsigned)grid),
-                       dim3(kDmaWM * kDmaWN * 64), 0, s, (const uint16_t*)A, lda, a_rows, (const uint16_t*)B, strideB,
-                       ldb, C, ldc, offsets, E, fixed_rows, N, K, n_tiles);
+    hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
+                       dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_rows, (const uint16_t*)B, strideB,
+                       ldb, Cm, ldc, offsets, E, fixed_rows, N, K, n_tiles);
     return hipGetLastError();
 }
 
-inline bool dma_ok(long lda, long ldb, int N, int K) {
-    return K % kDmaBK == 0 && K >= 2 * kDmaBK && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
+template <class C>
+bool dma_ok(long lda, long ldb, int N, int K) {
+    return K % C::BK == 0 && K >= 2 * C::BK && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
 }
 
 template <int EPI>
@@ -262,15 +273,18 @@ hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, lon
                         hipStream_t s) {
     switch (cfg) {
         case kTileM128:
-            if (dma_ok(lda, ldb, N, K))
-                return run_dma<EPI>(A, lda, nullptr, B, strideB, ldb, C, ldc, offsets, E, fixed_rows, max_rows, N, K,
-                                    s);
+            if (dma_ok<DmaLarge>(lda, ldb, N, K))
+                return run_dma<DmaLarge, EPI>(A, lda, nullptr, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                                              max_rows, N, K, s);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
         case kTileM64:
             return run_bf16<64, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                     max_rows, N, K, s);
         default:
+            if (dma_ok<DmaStream>(lda, ldb, N, K))
+                return run_dma<DmaStream, EPI>(A, lda, nullptr, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                                               max_rows, N, K, s);
             return run_bf16<16, 128, 64, 1, 4, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                     max_rows, N, K, s);
     }
@@ -291,12 +305,19 @@ hipError_t run_f32(const void* A, long lda, const void* B, long strideB, long ld
 }  // namespace
 
 bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt) {
-    return dt == kBF16 && cfg == kTileM128 && dma_ok(H, F, F, H);
+    if (dt != kBF16) return false;
+    if (cfg == kTileM128) return dma_ok<DmaLarge>(H, F, F, H);
+    if (cfg == kTileM16) return dma_ok<DmaStream>(H, F, F, H);
+    return false;
 }
 
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                                const void* W1, int H, int F, void* h, hipStream_t s) {
-    return run_dma<kEpiSiluOut>(x, H, row_token, W1, (long)H * F, F, h, F, offsets, E, 0, max_rows, F, H, s);
+                                const void* W1, int H, int F, TileCfg cfg, void* h, hipStream_t s) {
+    if (cfg == kTileM128)
+        return run_dma<DmaLarge, kEpiSiluOut>(x, H, row_token, W1, (long)H * F, F, h, F, offsets, E, 0, max_rows, F,
+                                              H, s);
+    return run_dma<DmaStream, kEpiSiluOut>(x, H, row_token, W1, (long)H * F, F, h, F, offsets, E, 0, max_rows, F, H,
+                                           s);
 }
 
 TileCfg choose_tile(long rows, int groups) {

@@ -119,7 +119,7 @@ int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* off
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
     if (row_token != nullptr)
-        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, h, s));
+        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, cfg, h, s));
     else
         MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, s));
     if (W1s != nullptr) {

@@ -42,7 +42,7 @@ TileCfg choose_tile(long rows, int groups);
 // through the row -> token map (the permute copy is then not needed).
 bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt);
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                                const void* W1, int H, int F, void* h, hipStream_t s);
+                                const void* W1, int H, int F, TileCfg cfg, void* h, hipStream_t s);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared,
                           int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
