@@ -155,6 +155,8 @@ def test_small_layers(dev, name, over):
     (50, 64, 16, 2, 0.0, 0.0),
     (77, 192, 24, 3, 0.1, 1.2),       # E < 32 padded columns, bias, drop
     (1, 1024, 40, 5, 0.0, 0.0),       # one token, many splits
+    (8, 2048, 128, 8, 0.0, 0.0),      # 32 splits: one workgroup per token in the reduction, eight loads a thread
+    (2, 4096, 32, 4, 0.0, 0.0),       # 64 splits over 32 padded expert columns
 ])
 def test_router_paths(dev, T, H, E, k, drop, zipf):
     I = gen.make_inputs("tiny", T=T, H=H, F=64, E=E, k=k, dtype="bf16", seed=95 + T, drop=drop, zipf=zipf)

@@ -243,6 +243,7 @@ struct Tile32 {
     static_assert(TM >= 1 && TN >= 1, "wave tile");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole KiB chunks per wave");
     static_assert(BN * 2 <= 1024 && BK * 2 <= 1024 && (BK == 32 || BK == 64), "row sizes");
+    static_assert(BN >= 128, "swz_b32 XORs chunk indices with up to 12: rows need >= 16 chunks of 8 columns");
     static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 

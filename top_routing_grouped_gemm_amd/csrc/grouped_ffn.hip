@@ -239,15 +239,17 @@ hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long l
 //  - DmaLarge: many rows per group (prefill). 256x256 tiles, 32-wide
 //    k-stages, a 4-stage ring, 8 waves; MFMA-bound when fed.
 //  - DmaStream: a few rows per group (decode). Each tile is one 32-row MFMA
-//    block against a 128-column weight slab; 64-wide k-stages in a 6-stage
-//    ring keep ~100 KB of weight loads in flight per CU, which is what
-//    streaming the expert weights at HBM rate needs.
+//    block against a 128-column weight slab; 64-wide k-stages in a 4-stage
+//    ring (80 KB) let two workgroups share a CU, so ~120 KB of weight loads
+//    stay in flight per CU and one workgroup's pipeline fill overlaps the
+//    other's tail (measured: 6 stages with one workgroup per CU streamed
+//    4.7 TB/s, 4 stages with two 5.5 TB/s).
 template <int BM_, int BN_, int BK_, int NS_, int WM_, int WN_>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
 };
 using DmaLarge = DmaCfg<256, 256, 32, 4, 4, 2>;
-using DmaStream = DmaCfg<32, 128, 64, 6, 1, 4>;
+using DmaStream = DmaCfg<32, 128, 64, 4, 1, 4>;
 
 template <class C, int EPI>
 hipError_t run_dma(const void* A, long lda, const int32_t* a_rows, const void* B, long strideB, long ldb, void* Cm,

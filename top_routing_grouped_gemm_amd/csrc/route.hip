@@ -396,20 +396,92 @@ __global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restric
     }
 }
 
-// Sum the S partial logits of each token in split order, add the bias, top-k.
-__global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restrict__ partial, int S, int T, int EP,
-                                                           const float* __restrict__ bias, int E, int k, float drop,
-                                                           int32_t* __restrict__ ids, float* __restrict__ wout) {
-    __shared__ float lg[4][256];
+// Sum the S partial logit rows of a token in split order, add the bias, top-k.
+// Two shapes, both issuing their loads several at a time (a serial walk over
+// S pays one L2/MALL round trip per split):
+//  - route_reduce_wave_kernel, few splits (large T): one wave per token, lane
+//    l owns experts l, l+64, ...; four splits' loads are in flight at once.
+//  - route_reduce_block_kernel, many splits (small T, long H): one workgroup
+//    per token; thread i owns expert i % EP and splits r, r+R, r+2R, ...
+//    (r = i / EP, R = 256 / EP), eight loads in flight; the R partial sums are
+//    then added in r order.
+// Each order is fixed, so the logits are deterministic.
+template <int EP>
+__global__ __launch_bounds__(256) void route_reduce_wave_kernel(const float* __restrict__ partial, int S, int T,
+                                                                const float* __restrict__ bias, int E, int k,
+                                                                float drop, int32_t* __restrict__ ids,
+                                                                float* __restrict__ wout) {
+    constexpr int Q = (EP + kWave - 1) / kWave;
+    __shared__ float lg[4][EP];
     const int wave = threadIdx.x / kWave, l = lane_id();
     const long t = (long)blockIdx.x * 4 + wave;
     if (t >= T) return;  // wave-uniform; no barrier follows
-    for (int e = l; e < E; e += kWave) {
-        float v = 0.0f;
-        for (int s = 0; s < S; ++s) v += partial[((long)s * T + t) * EP + e];
-        lg[wave][e] = v + (bias != nullptr ? bias[e] : 0.0f);
+    const float* p = partial + t * EP;
+    const long step = (long)T * EP;  // one split further
+    float acc[Q];
+#pragma unroll
+    for (int j = 0; j < Q; ++j) acc[j] = 0.0f;
+    int sp = 0;
+    for (; sp + 4 <= S; sp += 4) {
+        float q[4][Q];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < Q; ++j) {
+                const int e = j * kWave + l;
+                q[u][j] = e < EP ? p[(long)(sp + u) * step + e] : 0.0f;
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < Q; ++j) acc[j] += q[u][j];
+    }
+    for (; sp < S; ++sp)
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const int e = j * kWave + l;
+            if (e < EP) acc[j] += p[(long)sp * step + e];
+        }
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+        const int e = j * kWave + l;
+        if (e < E) lg[wave][e] = acc[j] + (bias != nullptr ? bias[e] : 0.0f);
     }
     topk_one_token(lg[wave], E, k, drop, t, ids, wout);
+}
+
+template <int EP>
+__global__ __launch_bounds__(256) void route_reduce_block_kernel(const float* __restrict__ partial, int S, int T,
+                                                                 const float* __restrict__ bias, int E, int k,
+                                                                 float drop, int32_t* __restrict__ ids,
+                                                                 float* __restrict__ wout) {
+    constexpr int R = 256 / EP;
+    __shared__ float part[R][EP];
+    __shared__ float lg[EP];
+    const long t = blockIdx.x;
+    const int e = threadIdx.x % EP, r = threadIdx.x / EP;
+    const float* p = partial + t * EP + e;
+    const long step = (long)T * EP;
+    float v = 0.0f;
+    int sp = r;
+    for (; sp + 7 * R < S; sp += 8 * R) {
+        float q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = p[(long)(sp + u * R) * step];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += q[u];
+    }
+    for (; sp < S; sp += R) v += p[(long)sp * step];
+    part[r][e] = v;
+    __syncthreads();
+    if (threadIdx.x >= kWave) return;  // wave 0 finishes; no barrier follows
+    for (int j = threadIdx.x; j < E; j += kWave) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) sum += part[rr][j];
+        lg[j] = sum + (bias != nullptr ? bias[j] : 0.0f);
+    }
+    topk_one_token(lg, E, k, drop, t, ids, wout);
 }
 
 // Splits of the H loop: the smallest power of two that gives >= 1024
@@ -440,8 +512,12 @@ hipError_t launch_v2(const uint16_t* x, const uint16_t* Wr, const float* bias, i
                        w, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(route_reduce_kernel, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)partial, S, T, EP, bias,
-                       E, k, drop, ids, w);
+    if (S >= 16)
+        hipLaunchKernelGGL(route_reduce_block_kernel<EP>, dim3(T), dim3(256), 0, s, (const float*)partial, S, T, bias,
+                           E, k, drop, ids, w);
+    else
+        hipLaunchKernelGGL(route_reduce_wave_kernel<EP>, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)partial, S,
+                           T, bias, E, k, drop, ids, w);
     return hipGetLastError();
 }
 
