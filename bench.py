@@ -145,6 +145,30 @@ def run_workload(name, steps, warmup, stage_reps):
     return I, res
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_ffn_hbm_traffic.txt")
+KERNEL_SOURCES = ("gemm_dma.hpp", "grouped_ffn.hip", "moe_common.hpp")
+
+
+def measured_traffic(key):
+    """HBM bytes per moe_grouped_ffn call from the committed rocprofv3 counter summary, or None when the
+    grouped-FFN kernel sources changed since those counters were taken (the summary records their SHA-256)."""
+    import hashlib
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    csrc = os.path.join(ROOT, "top_routing_grouped_gemm_amd", "csrc")
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in KERNEL_SOURCES)).hexdigest()
+    recorded = next((l.split(":", 1)[1].split()[0] for l in text.splitlines() if "kernel_source_sha256:" in l), None)
+    if recorded != sha:
+        return None
+    for l in text.splitlines():
+        if l.startswith(key + ":"):
+            return int(l.split(":", 1)[1])
+    return None
+
+
 def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
     """The fp64 oracle, as it stands, on the host cores: whole prefill batches, repeated until about 10 s."""
     import numpy as np
@@ -234,7 +258,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre["grouped_ffn_tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("traffic_prefill_bytes"),
+            "traffic_unit": "bytes per moe_grouped_ffn call (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
+            "algorithmic_bytes": pre["algorithmic_bytes"]["grouped_ffn"],
         },
         "prefill": pre,
     }
@@ -243,6 +269,7 @@ def main():
         wbytes = dec["experts_hit"] * 2 * Id.H * Id.F * Id.elem_bytes
         dec["weight_stream_gbs"] = round(wbytes / (dec["stages_ms"]["grouped_ffn"] * 1e-3) / 1e9, 1)
         dec["weight_stream_hbm_frac"] = round(dec["weight_stream_gbs"] / PEAK_HBM_GBS, 4)
+        dec["grouped_ffn_traffic_bytes"] = measured_traffic("traffic_decode_bytes")
         line["decode"] = dec
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle) ...")
