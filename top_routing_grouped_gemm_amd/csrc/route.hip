@@ -10,7 +10,7 @@
 // bf16: one workgroup (4 waves) takes 16 or 32 tokens; the logits block is a
 // small GEMM on the matrix cores (bf16 products, fp32 accumulation) with Wr
 // transposed into LDS. The fp32 logits then go to LDS and each wave runs the
-// top-k of one token at a time with wave64 shuffle reductions; the logits are
+// top-k of one token at a time (a ballot-based radix select); the logits are
 // never written to memory.
 #include <float.h>
 #include <math.h>
@@ -27,68 +27,113 @@ constexpr int kRouteBK = 32;
 constexpr int kRouteS = kRouteBK + 8;  // LDS row stride (bf16 elements)
 constexpr int kQMax = 16;              // experts per lane: E <= 1024
 
-// Top-k of one token whose E logits sit in LDS at lg[0..E). Whole wave.
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+__device__ __forceinline__ uint32_t ord_key(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Top-k of one token whose E logits sit in LDS at lg[0..E) (E <= 64*Q), one
+// whole wave; lane l holds experts l, l+64, ... (ascending id = q-major order).
+//  1. Radix select: the k-th largest key tau is built bit by bit from the top,
+//     keeping a bit when at least k keys are >= the candidate (a wave ballot
+//     and a popcount per expert slice: no cross-lane shuffles).
+//  2. Keys > tau are selected; keys == tau fill the remaining places in
+//     ascending expert id (ties go to the lower id).
+//  3. Slot = rank of the expert id among the selected (ballot prefix counts).
+//  4. Softmax over the selected logits, optional drop (w < drop -> 0) and
+//     renormalisation; a kept weight is clamped to >= FLT_MIN so that 0.0f
+//     always means dropped.
+template <int Q>
+__device__ void topk_select(const float* lg, int E, int k, float drop, long t, int32_t* __restrict__ ids,
+                            float* __restrict__ wout) {
+    const int l = lane_id();
+    float v[Q];
+    uint32_t key[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = q * kWave + l;
+        v[q] = e < E ? lg[e] : -INFINITY;
+        key[q] = e < E ? ord_key(v[q] + 0.0f) : 0u;  // -0 keyed as +0 (equal logits tie); 0 is below every logit
+    }
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) c += __popcll(__ballot(key[q] >= cand));
+        if (c >= k) tau = cand;
+    }
+    int n_gt = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) n_gt += __popcll(__ballot(key[q] > tau));
+    const int need = k - n_gt;  // >= 1 places left for keys equal to tau
+    const unsigned long long below = (1ull << l) - 1ull;
+    bool sel[Q];
+    int ties = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const unsigned long long m = __ballot(key[q] == tau);
+        const int before = ties + __popcll(m & below);
+        sel[q] = key[q] > tau || (key[q] == tau && before < need);
+        ties += __popcll(m);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (sel[q]) mx = fmaxf(mx, v[q]);
+    mx = wave_max(mx);
+    float p[Q], ps = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        p[q] = sel[q] ? expf(v[q] - mx) : 0.0f;
+        ps += p[q];
+    }
+    const float sum = wave_sum(ps);
+    bool kept[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        p[q] = p[q] / sum;
+        kept[q] = sel[q];
+    }
+    if (drop > 0.0f) {
+        float ks = 0.0f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            kept[q] = sel[q] && !(p[q] < drop);
+            if (!kept[q]) p[q] = 0.0f;
+            ks += p[q];
+        }
+        const float kept_sum = wave_sum(ks);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) p[q] = p[q] / kept_sum;
+    }
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const unsigned long long m = __ballot(sel[q]);
+        if (sel[q]) {
+            const int slot = base + __popcll(m & below);
+            ids[t * k + slot] = q * kWave + l;
+            wout[t * k + slot] = kept[q] ? fmaxf(p[q], FLT_MIN) : 0.0f;
+        }
+        base += __popcll(m);
+    }
+}
+
 __device__ void topk_one_token(const float* lg, int E, int k, float drop, long t, int32_t* __restrict__ ids,
                                float* __restrict__ wout) {
-    const int l = lane_id();
-    float v[kQMax];
-#pragma unroll
-    for (int q = 0; q < kQMax; ++q) {
-        const int e = q * kWave + l;
-        v[q] = (e < E) ? lg[e] : -INFINITY;
-    }
-    int my_id = 0x7fffffff;
-    float my_v = -INFINITY;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int q = 0; q < kQMax; ++q) {
-            const int e = q * kWave + l;
-            if (e < E && (v[q] > bv || (v[q] == bv && e < bi))) {
-                bv = v[q];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, kWave);
-            const int oi = __shfl_xor(bi, o, kWave);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (l == j) {
-            my_id = bi;
-            my_v = bv;
-        }
-        if ((bi & (kWave - 1)) == l) {
-            const int qs = bi / kWave;
-#pragma unroll
-            for (int q = 0; q < kQMax; ++q)
-                if (q == qs) v[q] = -INFINITY;
-        }
-    }
-    // softmax over the k selected logits; lane 0 holds the largest
-    const float m = __shfl(my_v, 0, kWave);
-    const bool sel = l < k;
-    float p = sel ? expf(my_v - m) : 0.0f;
-    float w = p / wave_sum(p);
-    bool kept = sel;
-    if (drop > 0.0f) {
-        kept = sel && !(w < drop);
-        const float wk = kept ? w : 0.0f;
-        w = wk / wave_sum(wk);
-    }
-    if (kept) w = fmaxf(w, FLT_MIN);  // a kept slot never carries 0.0f
-    // slot = rank of the expert id among the k selected
-    int rank = 0;
-    for (int i = 0; i < k; ++i) rank += (__shfl(my_id, i, kWave) < my_id);
-    if (sel) {
-        ids[t * k + rank] = my_id;
-        wout[t * k + rank] = kept ? w : 0.0f;
-    }
+    if (E <= kWave) topk_select<1>(lg, E, k, drop, t, ids, wout);
+    else if (E <= 2 * kWave) topk_select<2>(lg, E, k, drop, t, ids, wout);
+    else if (E <= 4 * kWave) topk_select<4>(lg, E, k, drop, t, ids, wout);
+    else if (E <= 8 * kWave) topk_select<8>(lg, E, k, drop, t, ids, wout);
+    else topk_select<kQMax>(lg, E, k, drop, t, ids, wout);
 }
 
 template <int MT, int NTW, bool VEC>
