@@ -18,48 +18,71 @@ namespace moe {
 
 namespace {
 
-// Slots are processed 8 at a time with every load of a chunk issued before
-// any of its FMAs, so one thread keeps up to 8 row gathers in flight.
+// Each thread owns up to two 4-float column groups (c and c + 256) and
+// processes slots 8 at a time with every load of a chunk issued before any of
+// its FMAs, so up to 16 row gathers are in flight per thread. Accumulation is
+// fp32 in slot order; dropped slots (w == 0) add nothing.
+template <bool OUT_BF16>
+__device__ __forceinline__ void combine_store(float4 acc, void* __restrict__ y, long idx) {
+    if (OUT_BF16) {
+        u32x2 pk = {pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
+        ((u32x2*)y)[idx] = pk;
+    } else {
+        ((float4*)y)[idx] = acc;
+    }
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, const float4* __restrict__ ysh,
                                                       int H4, int k, void* __restrict__ y) {
     const long t = blockIdx.x;
-    for (int c = threadIdx.x; c < H4; c += 256) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = threadIdx.x; c0 < H4; c0 += 512) {
+        const int c1 = c0 + 256;
+        const bool two = c1 < H4;
+        float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
         for (int j0 = 0; j0 < k; j0 += 8) {
-            float4 v[8];
+            float4 v0[8], v1[8];
             float ww[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = j0 + u;
                 const int r = j < k ? inv[t * k + j] : -1;
                 ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
-                v[u] = r >= 0 ? y_perm[(long)r * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4* row = y_perm + (long)(r >= 0 ? r : 0) * H4;
+                v0[u] = r >= 0 ? row[c0] : make_float4(0.f, 0.f, 0.f, 0.f);
+                v1[u] = (r >= 0 && two) ? row[c1] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                if (j0 + u < k && ww[u] != 0.0f) {  // slot order; dropped slots add nothing
-                    acc.x = fmaf(ww[u], v[u].x, acc.x);
-                    acc.y = fmaf(ww[u], v[u].y, acc.y);
-                    acc.z = fmaf(ww[u], v[u].z, acc.z);
-                    acc.w = fmaf(ww[u], v[u].w, acc.w);
+                if (j0 + u < k && ww[u] != 0.0f) {
+                    a0.x = fmaf(ww[u], v0[u].x, a0.x);
+                    a0.y = fmaf(ww[u], v0[u].y, a0.y);
+                    a0.z = fmaf(ww[u], v0[u].z, a0.z);
+                    a0.w = fmaf(ww[u], v0[u].w, a0.w);
+                    a1.x = fmaf(ww[u], v1[u].x, a1.x);
+                    a1.y = fmaf(ww[u], v1[u].y, a1.y);
+                    a1.z = fmaf(ww[u], v1[u].z, a1.z);
+                    a1.w = fmaf(ww[u], v1[u].w, a1.w);
                 }
             }
         }
         if (ysh != nullptr) {
-            const float4 v = ysh[t * H4 + c];
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+            const float4 s0 = ysh[t * H4 + c0];
+            a0.x += s0.x;
+            a0.y += s0.y;
+            a0.z += s0.z;
+            a0.w += s0.w;
+            if (two) {
+                const float4 s1 = ysh[t * H4 + c1];
+                a1.x += s1.x;
+                a1.y += s1.y;
+                a1.z += s1.z;
+                a1.w += s1.w;
+            }
         }
-        if (OUT_BF16) {
-            u32x2 pk = {pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
-            ((u32x2*)y)[t * H4 + c] = pk;
-        } else {
-            ((float4*)y)[t * H4 + c] = acc;
-        }
+        combine_store<OUT_BF16>(a0, y, t * H4 + c0);
+        if (two) combine_store<OUT_BF16>(a1, y, t * H4 + c1);
     }
 }
 

@@ -59,7 +59,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ partia
     const int b0 = g * bpg, b1 = min(n_blocks, b0 + bpg);
     if (act) {
         int s = 0;
-        for (int b = b0; b < b1; ++b) s += partial[(long)b * E + e];
+        for (int b = b0; b < b1; b += 16) {  // 16 independent loads in flight
+            int c[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) c[u] = (b + u < b1) ? partial[(long)(b + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) s += c[u];
+        }
         gs[g * E + e] = s;
     }
     __syncthreads();
