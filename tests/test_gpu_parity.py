@@ -224,9 +224,15 @@ def test_combine_oracle_fed(dev):
     assert np.abs(y.double().cpu().numpy() - ref.y).max() <= 1e-5 * np.abs(ref.y).max()
 
 
-def test_permute_oracle_fed(dev):
+@pytest.mark.parametrize("T,E", [
+    (777, 37),     # 3108 assignments: count / scan / index kernels
+    (256, 37),     # 1024 assignments: the single-workgroup dispatch, at its limit
+    (257, 1000),   # 1028 assignments just past it, E near the maximum
+    (200, 1000),   # 800 assignments over 1000 experts in one workgroup
+])
+def test_permute_oracle_fed(dev, T, E):
     """Oracle-fed permute: ids/weights from the oracle (with drops)."""
-    I = gen.make_inputs("tiny", T=777, H=64, F=32, E=37, k=4, dtype="bf16", seed=92, drop=0.1)
+    I = gen.make_inputs("tiny", T=T, H=64, F=32, E=E, k=4, dtype="bf16", seed=92, drop=0.1)
     r = oracle.route(I.f64(I.x), I.f64(I.Wr), None, I.k, I.drop)
     dref = oracle.dispatch(r.ids, r.keep, I.E)
     x = gen.storage_to_torch(I.x, "bf16").to(dev)

@@ -7,7 +7,8 @@
 // token). Section "单机MoE执行流水线": the permute reads token vectors, writes
 // them in expert order and records an inverse map for the combine.
 //
-// Order is fixed by (expert, token), never by atomics:
+// Order is fixed by (expert, token), never by atomics (batches of at most
+// 1024 assignments run count, scan and index in one workgroup instead):
 //   count  - each workgroup histograms one chunk of 256 assignments in LDS;
 //   scan   - one workgroup turns the [chunk][expert] histograms into the
 //            first output row of every (chunk, expert) pair and writes the
@@ -25,6 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kMaxE = 1024;
+static_assert(kMaxE == kSmallAssign, "dispatch_small_kernel scans one expert per thread");
 
 __global__ __launch_bounds__(kDispatchChunk) void count_kernel(const int32_t* __restrict__ ids,
                                                                const float* __restrict__ w, int n_assign, int E,
@@ -140,6 +142,76 @@ __global__ __launch_bounds__(kDispatchChunk) void index_kernel(const int32_t* __
     }
 }
 
+// All of count, scan and index in one workgroup of 1024 threads, for batches
+// of at most 1024 assignments (decode): thread a ranks assignment a within its
+// expert (wave ballots over the id bits), LDS turns the per-wave counts into
+// wave prefixes and expert offsets, and the same order as the three-kernel
+// path results (expert, then token). Saves two launches where latency, not
+// bandwidth, is the cost.
+__global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int32_t* __restrict__ ids,
+                                                                      const float* __restrict__ w, int n_assign,
+                                                                      int k, int E, int ebits,
+                                                                      int32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ row_token,
+                                                                      int32_t* __restrict__ inv) {
+    constexpr int NW = kSmallAssign / kWave;
+    __shared__ int wc[NW][kMaxE];  // per-wave counts, then per-wave first rank
+    __shared__ int eoff[kMaxE];    // expert totals, then expert offsets
+    __shared__ int wsum[NW];
+    const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+    for (int i = tid; i < NW * E; i += kSmallAssign) (&wc[0][0])[(i / E) * kMaxE + (i % E)] = 0;
+    const int a = tid;
+    const bool valid = a < n_assign;
+    const int id = valid ? ids[a] : 0;
+    const bool kept = valid && w[a] != 0.0f && (unsigned)id < (unsigned)E;  // out-of-range ids: dropped
+    const int e = kept ? id : 0;
+    unsigned long long same = __ballot(kept);
+    for (int b = 0; b < ebits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+    }
+    const unsigned long long below = (l == 0) ? 0ull : (~0ull >> (kWave - l));
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    __syncthreads();
+    if (kept && rank == 0) wc[wv][e] = cnt;
+    __syncthreads();
+    for (int x = tid; x < E; x += kSmallAssign) {  // wave prefixes per expert, expert totals
+        int run = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int c = wc[i][x];
+            wc[i][x] = run;
+            run += c;
+        }
+        eoff[x] = run;
+    }
+    __syncthreads();
+    const int v = tid < E ? eoff[tid] : 0;  // E <= kMaxE == kSmallAssign: one expert per thread
+    const int incl = wave_incl_scan(v);
+    if (l == kWave - 1) wsum[wv] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int i = 0; i < wv; ++i) wbase += wsum[i];
+    const int excl = wbase + incl - v;
+    if (tid < E) {
+        eoff[tid] = excl;
+        offsets[tid] = excl;
+    }
+    if (tid == E - 1) offsets[E] = excl + v;
+    __syncthreads();
+    if (valid) {
+        if (kept) {
+            const int r = eoff[e] + wc[wv][e] + rank;
+            row_token[r] = a / k;
+            inv[a] = r;
+        } else {
+            inv[a] = -1;
+        }
+    }
+}
+
 // Each wave copies RPW consecutive destination rows: the source token of each
 // row is read once (wave-uniform), then every 16-byte load of all RPW rows is
 // issued before the stores.
@@ -179,6 +251,15 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const u32x4* __restrict_
 hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial, hipStream_t s) {
     const int nb = dispatch_blocks(n_assign);
     hipLaunchKernelGGL(count_kernel, dim3(nb), dim3(kDispatchChunk), 0, s, ids, w, n_assign, E, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_small(const int32_t* ids, const float* w, int n_assign, int k, int E, int32_t* offsets,
+                                 int32_t* row_token, int32_t* inv, hipStream_t s) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallAssign), 0, s, ids, w, n_assign, k, E, ebits, offsets,
+                       row_token, inv);
     return hipGetLastError();
 }
 

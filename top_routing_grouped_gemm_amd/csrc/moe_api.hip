@@ -101,9 +101,13 @@ int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, in
                     moe_dtype_t dt, void* x_perm, int32_t* offsets, int32_t* row_token, int32_t* inv,
                     int32_t* partial, bool copy_rows, hipStream_t s) {
     const int n = T * k;
-    MOE_TRY(moe::launch_count(ids, w, n, E, partial, s));
-    MOE_TRY(moe::launch_scan(partial, moe::dispatch_blocks(n), E, offsets, s));
-    MOE_TRY(moe::launch_index(ids, w, partial, n, k, E, row_token, inv, s));
+    if (n <= moe::kSmallAssign) {
+        MOE_TRY(moe::launch_dispatch_small(ids, w, n, k, E, offsets, row_token, inv, s));
+    } else {
+        MOE_TRY(moe::launch_count(ids, w, n, E, partial, s));
+        MOE_TRY(moe::launch_scan(partial, moe::dispatch_blocks(n), E, offsets, s));
+        MOE_TRY(moe::launch_index(ids, w, partial, n, k, E, row_token, inv, s));
+    }
     if (copy_rows) MOE_TRY(moe::launch_copy_rows(x, row_token, offsets, E, n, (int)(H * elem_bytes(dt)), x_perm, s));
     return MOE_OK;
 }

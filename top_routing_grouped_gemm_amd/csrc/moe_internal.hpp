@@ -11,6 +11,7 @@ namespace moe {
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
 constexpr int kDispatchChunk = 256;  // assignments per dispatch workgroup
+constexpr int kSmallAssign = 1024;   // batches up to this many assignments dispatch in one workgroup
 
 // Ragged GEMM tile shapes, chosen on the host from the mean rows per expert.
 enum TileCfg { kTileM16 = 0, kTileM64 = 1, kTileM128 = 2 };
@@ -26,6 +27,8 @@ hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T,
 hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial,
                         hipStream_t s);
 hipError_t launch_scan(int32_t* partial, int n_blocks, int E, int32_t* offsets, hipStream_t s);
+hipError_t launch_dispatch_small(const int32_t* ids, const float* w, int n_assign, int k, int E, int32_t* offsets,
+                                 int32_t* row_token, int32_t* inv, hipStream_t s);
 hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* partial, int n_assign, int k,
                         int E, int32_t* row_token, int32_t* inv, hipStream_t s);
 hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32_t* offsets, int E,
