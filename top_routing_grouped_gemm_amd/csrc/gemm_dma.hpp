@@ -196,15 +196,24 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
 // and columns past N get an out-of-range offset and are dropped by the buffer
 // descriptor, so no store sits behind a branch and every lane issues the same
 // number of stores.
+//
+// c_cap > 0 selects the k-blocked layout [N/32][c_cap][32] for C (N % 32 == 0,
+// N * c_cap * element bytes < 2^31): element (r, n) at ((n/32)*c_cap + r)*32
+// + n%32. Consecutive rows of one 32-column block are then adjacent, so the
+// next GEMM's A-tile loads of 32 k-values over consecutive rows are one
+// contiguous run instead of 64-byte pieces of separate rows. Rows past the
+// group are dropped by an explicit out-of-range offset in that layout.
 template <int TM, int TN, int WTM, int WTN, int EPI>
-__device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, long ldc, int rb, int re, int n0, int N,
-                                             int wm, int wn) {
+__device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, long ldc, long c_cap, int rb, int re,
+                                             int n0, int N, int wm, int wn) {
     constexpr int ES = EPI == 0 ? 2 : 4;
     const int l = lane_id();
     const long ldc_b = ldc * ES;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (uint8_t*)C + (long)rb * ldc_b + (long)n0 * ES, (short)0, (int)((long)(re - rb) * ldc_b - (long)n0 * ES),
-        0x00020000);
+    const bool blocked = c_cap > 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        blocked ? __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)((long)N * c_cap * ES), 0x00020000)
+                : __builtin_amdgcn_make_buffer_rsrc((uint8_t*)C + (long)rb * ldc_b + (long)n0 * ES, (short)0,
+                                                    (int)((long)(re - rb) * ldc_b - (long)n0 * ES), 0x00020000);
     const int c0 = (l & 31) & ~3, m = l & 3;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -217,7 +226,13 @@ __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, lon
                 float v[4] = {acc[i][jj][4 * p], acc[i][jj][4 * p + 1], acc[i][jj][4 * p + 2], acc[i][jj][4 * p + 3]};
                 quad_transpose(v);
                 const int rowrel = wm * WTM + i * 32 + 8 * p + 4 * (l >> 5) + m;
-                const int off = col_ok ? rowrel * (int)ldc_b + colrel * ES : 0x7ffffff0;
+                int off;
+                if (blocked)
+                    off = (col_ok && rowrel < re - rb)
+                              ? (int)((((long)(n0 + colrel - c0) >> 5) * c_cap + rb + rowrel) * (32 * ES) + c0 * ES)
+                              : 0x7ffffff0;
+                else
+                    off = col_ok ? rowrel * (int)ldc_b + colrel * ES : 0x7ffffff0;
                 if (EPI == 0) {
                     typedef __attribute__((ext_vector_type(2))) unsigned u2;
                     const u2 pk = {pack_bf16x2(silu_f32(v[0]), silu_f32(v[1])),
@@ -249,11 +264,15 @@ struct Tile32 {
 
 // a_rows (nullable): A row of output row r is a_rows[r] (the permute folded
 // into the A-tile loads: A is then x[T,H] and a_rows the row -> token map).
+// A element (r, k) sits at A[r*lda + (k/BK)*BK*a_kstep + k%BK]: row-major is
+// lda = K, a_kstep = 1; the k-blocked layout written by store_tile32 with
+// c_cap = cap is lda = 32, a_kstep = cap (BK == 32 only).
+// c_cap: 0 for a row-major C with leading dimension ldc, else the k-blocked C.
 template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t* __restrict__ A, long lda,
-                                                                 const int32_t* __restrict__ a_rows,
+                                                                 long a_kstep, const int32_t* __restrict__ a_rows,
                                                                  const uint16_t* __restrict__ B, long strideB,
-                                                                 long ldb, void* __restrict__ C, long ldc,
+                                                                 long ldb, void* __restrict__ C, long ldc, long c_cap,
                                                                  const int32_t* __restrict__ offsets, int E,
                                                                  int fixed_rows, int N, int K, int n_tiles) {
     using Tl = Tile32<BM, BN, BK, NS, WM, WN>;
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     auto issue = [&](int stage, int k0) {
         const uint32_t b0 = (uint32_t)(uintptr_t)(ring + stage * STAGE) + uwave * 1024;
 #pragma unroll
-        for (int i = 0; i < Tl::A_CHUNKS; ++i) lds_dma16(a_src[i] + k0, b0 + i * 1024 * NW);
+        for (int i = 0; i < Tl::A_CHUNKS; ++i) lds_dma16(a_src[i] + (long)k0 * a_kstep, b0 + i * 1024 * NW);
 #pragma unroll
         for (int i = 0; i < Tl::B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * ldb, b0 + A_BYTES + i * 1024 * NW);
     };
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     if (!active) return;
     mma(fa[1], fb[1]);
 
-    store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, rb, re, n0, N, wm, wn);
+    store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, wm, wn);
 }
 
 }  // namespace dma

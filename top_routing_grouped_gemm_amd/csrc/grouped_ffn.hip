@@ -251,16 +251,18 @@ struct DmaCfg {
 using DmaLarge = DmaCfg<256, 256, 32, 4, 4, 2>;
 using DmaStream = DmaCfg<32, 128, 64, 4, 1, 4>;
 
+// a_kstep / c_cap: see gemm32_kernel (1 / 0 for row-major A / C).
 template <class C, int EPI>
-hipError_t run_dma(const void* A, long lda, const int32_t* a_rows, const void* B, long strideB, long ldb, void* Cm,
-                   long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K, hipStream_t s) {
+hipError_t run_dma(const void* A, long lda, long a_kstep, const int32_t* a_rows, const void* B, long strideB, long ldb,
+                   void* Cm, long ldc, long c_cap, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N,
+                   int K, hipStream_t s) {
     const int n_tiles = (N + C::BN - 1) / C::BN;
     // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
     const long grid = max_mtiles(C::BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
-                       dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_rows, (const uint16_t*)B, strideB,
-                       ldb, Cm, ldc, offsets, E, fixed_rows, N, K, n_tiles);
+                       dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_kstep, a_rows, (const uint16_t*)B,
+                       strideB, ldb, Cm, ldc, c_cap, offsets, E, fixed_rows, N, K, n_tiles);
     return hipGetLastError();
 }
 
@@ -269,14 +271,23 @@ bool dma_ok(long lda, long ldb, int N, int K) {
     return K % C::BK == 0 && K >= 2 * C::BK && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
 }
 
+// h_cap > 0: the k-blocked h layout (W1 writes it as C, W2 reads it as A);
+// only the large direct-to-LDS shape takes it (h_blocked decides).
 template <int EPI>
 hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, long strideB, long ldb, void* C,
                         long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K,
-                        hipStream_t s) {
+                        long h_cap, hipStream_t s) {
+    if (h_cap > 0) {
+        if (EPI == kEpiSiluOut)  // W1: C = h blocked
+            return run_dma<DmaLarge, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, h_cap, offsets, E, fixed_rows,
+                                          max_rows, N, K, s);
+        return run_dma<DmaLarge, EPI>(A, 32, h_cap, nullptr, B, strideB, ldb, C, ldc, 0, offsets, E, fixed_rows,
+                                      max_rows, N, K, s);  // W2: A = h blocked
+    }
     switch (cfg) {
         case kTileM128:
             if (dma_ok<DmaLarge>(lda, ldb, N, K))
-                return run_dma<DmaLarge, EPI>(A, lda, nullptr, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                return run_dma<DmaLarge, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, 0, offsets, E, fixed_rows,
                                               max_rows, N, K, s);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
@@ -285,7 +296,7 @@ hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, lon
                                                     max_rows, N, K, s);
         default:
             if (dma_ok<DmaStream>(lda, ldb, N, K))
-                return run_dma<DmaStream, EPI>(A, lda, nullptr, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                return run_dma<DmaStream, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, 0, offsets, E, fixed_rows,
                                                max_rows, N, K, s);
             return run_bf16<16, 128, 64, 1, 4, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                     max_rows, N, K, s);
@@ -314,12 +325,19 @@ bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt) {
 }
 
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                                const void* W1, int H, int F, TileCfg cfg, void* h, hipStream_t s) {
+                                const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s) {
     if (cfg == kTileM128)
-        return run_dma<DmaLarge, kEpiSiluOut>(x, H, row_token, W1, (long)H * F, F, h, F, offsets, E, 0, max_rows, F,
-                                              H, s);
-    return run_dma<DmaStream, kEpiSiluOut>(x, H, row_token, W1, (long)H * F, F, h, F, offsets, E, 0, max_rows, F, H,
-                                           s);
+        return run_dma<DmaLarge, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, h_cap, offsets, E, 0,
+                                              max_rows, F, H, s);
+    return run_dma<DmaStream, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, 0, offsets, E, 0, max_rows,
+                                           F, H, s);
+}
+
+long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt) {
+    if (dt != kBF16 || cfg != kTileM128 || F % 32 != 0) return 0;
+    if (!dma_ok<DmaLarge>(H, F, F, H) || !dma_ok<DmaLarge>(F, H, H, F)) return 0;
+    if (cap * F * 2 > 0x7fff0000L) return 0;  // 32-bit buffer offsets
+    return cap;
 }
 
 TileCfg choose_tile(long rows, int groups) {
@@ -330,18 +348,20 @@ TileCfg choose_tile(long rows, int groups) {
 }
 
 hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed_rows, int max_rows, const void* W1,
-                         int H, int F, Dtype dt, void* h, TileCfg cfg, hipStream_t s) {
+                         int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s) {
     const long strideB = (offsets == nullptr) ? 0 : (long)H * F;
     if (dt == kBF16)
-        return run_bf16_cfg<kEpiSiluOut>(cfg, A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H, s);
+        return run_bf16_cfg<kEpiSiluOut>(cfg, A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H,
+                                         h_cap, s);
     return run_f32<kEpiSiluOut>(A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H, s);
 }
 
 hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
-                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, hipStream_t s) {
+                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s) {
     const long strideB = (offsets == nullptr) ? 0 : (long)F * H;
     if (dt == kBF16)
-        return run_bf16_cfg<kEpiF32Out>(cfg, h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, s);
+        return run_bf16_cfg<kEpiF32Out>(cfg, h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, h_cap,
+                                        s);
     return run_f32<kEpiF32Out>(h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, s);
 }
 

@@ -122,18 +122,20 @@ int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* off
     const Dtype d = (Dtype)dt;
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
+    const long hc = moe::h_blocked(cfg, H, F, rows, d);  // h layout shared by the W1 and W2 launches
     if (row_token != nullptr)
-        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, cfg, h, s));
+        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, cfg, hc, h, s));
     else
-        MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, s));
+        MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, hc, s));
     if (W1s != nullptr) {
         void* hs = base + L.h_sh;
         const moe::TileCfg cs = moe::choose_tile(T, 1);
-        MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, s));
-        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, s));
-        MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, s));
+        const long hsc = moe::h_blocked(cs, H, Fs, T, d);
+        MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, hsc, s));
+        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, hc, s));
+        MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, hsc, s));
     } else {
-        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, s));
+        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, hc, s));
     }
     return MOE_OK;
 }

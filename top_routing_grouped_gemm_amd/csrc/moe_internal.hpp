@@ -36,16 +36,21 @@ hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32
 
 // Grouped FFN. Rows of group e are [offsets[e], offsets[e+1]); with offsets == NULL there
 // is a single group of rows [0, fixed_rows) (the shared expert).
+// h_cap: 0 for a row-major h[rows, F]; > 0 (from h_blocked) for the k-blocked
+// h[F/32][h_cap][32] that the W1 launch writes and the W2 launch reads.
 hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed_rows, int max_rows,
-                         const void* W1, int H, int F, Dtype dt, void* h, TileCfg cfg, hipStream_t s);
+                         const void* W1, int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s);
 hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
-                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, hipStream_t s);
+                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s);
+// Row capacity for the k-blocked h (the large direct-to-LDS shape with bf16
+// and F % 32 == 0), or 0 for row-major.
+long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt);
 TileCfg choose_tile(long rows, int groups);
 // Whether the W1 launch for this tile shape can read token rows of x directly
 // through the row -> token map (the permute copy is then not needed).
 bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt);
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                                const void* W1, int H, int F, TileCfg cfg, void* h, hipStream_t s);
+                                const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared,
                           int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
