@@ -61,6 +61,7 @@ def stage_times(d, I, reps):
     fws = torch.empty(moe.moe_ffn_workspace_bytes(T, F, E, k, I.Fs, d["x"].dtype), dtype=torch.uint8, device=dev)
     y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev) if I.Fs else None
 
     def route():
         moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop, topk_ids=ids, topk_w=w)
@@ -68,11 +69,12 @@ def stage_times(d, I, reps):
     def permute():
         moe.moe_permute(d["x"], ids, w, E, x_perm=x_perm, expert_offsets=off, row_token=row_token, inv=inv, ws=pws)
 
-    def ffn():
-        moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm, ws=fws)
+    def ffn():  # routed experts, plus the shared expert when the workload has one
+        moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm, x=d["x"], W1s=d["W1s"], W2s=d["W2s"],
+                            y_shared=y_sh, ws=fws)
 
     def combine():
-        moe.moe_combine(y_perm, inv, w, y=y)
+        moe.moe_combine(y_perm, inv, w, y_shared=y_sh, y=y)
 
     route()
     permute()
@@ -88,11 +90,13 @@ def bytes_model(I, A, experts_hit):
     """Algorithmic HBM bytes per call of each stage (each array read or written once)."""
     b = I.elem_bytes
     T, H, F, E, k = I.T, I.H, I.F, I.E, I.k
+    Fs = I.Fs
+    shared_ffn = (2 * H * Fs * b + T * H * b + T * H * 4) if Fs else 0  # W1s, W2s, x read, y_shared written
     return {
         "route": T * H * b + H * E * b + T * k * 8,
         "permute": T * H * b + A * H * b + T * k * 8 * 2 + A * 4,
-        "grouped_ffn": experts_hit * 2 * H * F * b + A * H * b + A * H * 4,
-        "combine": A * H * 4 + T * k * 8 + T * H * 4,
+        "grouped_ffn": experts_hit * 2 * H * F * b + A * H * b + A * H * 4 + shared_ffn,
+        "combine": A * H * 4 + T * k * 8 + T * H * 4 + (T * H * 4 if Fs else 0),
     }
 
 
@@ -126,7 +130,7 @@ def run_workload(name, steps, warmup, stage_reps):
     ms = (time.perf_counter() - t) * 1e3 / steps
     st, A, counts = stage_times(d, I, stage_reps)
     hit = int((counts > 0).sum())
-    flops = 4.0 * A * I.H * I.F
+    flops = 4.0 * A * I.H * I.F + 4.0 * I.T * I.H * I.Fs  # routed experts + shared expert
     byts = bytes_model(I, A, hit)
     res = {
         "T": I.T, "H": I.H, "F": I.F, "E": I.E, "k": I.k, "A": A, "experts_hit": hit,
@@ -137,6 +141,9 @@ def run_workload(name, steps, warmup, stage_reps):
         "stage_gbs": {k: round(byts[k] / (st[k] * 1e-3) / 1e9, 1) for k in st},
         "stage_hbm_frac": {k: round(byts[k] / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k in st},
         "grouped_ffn_tflops": flops / (st["grouped_ffn"] * 1e-3) / 1e12,
+        "grouped_ffn_mfma_frac": round(flops / (st["grouped_ffn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "weight_stream_gbs": round((hit * 2 * I.H * I.F + 2 * I.H * I.Fs) * I.elem_bytes
+                                   / (st["grouped_ffn"] * 1e-3) / 1e9, 1),
         "grouped_ffn_flops": flops,
         "algorithmic_bytes": byts,
     }
@@ -205,8 +212,8 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one workload only (for profiling runs); prints its stage times")
+    ap.add_argument("--only", choices=["tiny", "decode", "prefill", "mixtral_shared", "skew"], default=None,
+                    help="time one workload only (profiling runs and the per-workload table); prints its stage times")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

@@ -85,10 +85,11 @@ __device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row 
 __device__ __forceinline__ int swz_b(int row, int chunk) { return chunk ^ (2 * ((row & 3) + 4 * ((row >> 3) & 1))); }
 
 // Map this workgroup to (expert, M-tile rows, N-tile). All waves compute the
-// same answer; returns false for workgroups past the last tile.
+// same answer; returns false for workgroups past the last tile. Only groups
+// with rmin <= rows < rmax get tiles (another launch takes the others).
 template <int BM>
 __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, int E, int fixed_rows, int n_tiles,
-                                         int& e_out, int& rb, int& re, int& nt) {
+                                         int rmin, int rmax, int& e_out, int& rb, int& re, int& nt) {
     const int l = lane_id();
     int total_m, incl = 0, s = 0, per = 1;
     if (offsets == nullptr) {
@@ -98,7 +99,7 @@ __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, in
         const int e0 = l * per, e1 = min(E, e0 + per);
         for (int e = e0; e < e1; ++e) {
             const int c = offsets[e + 1] - offsets[e];
-            s += (c + BM - 1) / BM;
+            s += (c >= rmin && c < rmax) ? (c + BM - 1) / BM : 0;
         }
         incl = wave_incl_scan(s);
         total_m = __shfl(incl, kWave - 1, kWave);
@@ -124,7 +125,7 @@ __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, in
     int e = eL0;
     for (; e < eL1; ++e) {
         const int c = offsets[e + 1] - offsets[e];
-        const int tt = (c + BM - 1) / BM;
+        const int tt = (c >= rmin && c < rmax) ? (c + BM - 1) / BM : 0;
         if (mt < before + tt) break;
         before += tt;
     }
@@ -274,14 +275,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ B, long strideB,
                                                                  long ldb, void* __restrict__ C, long ldc, long c_cap,
                                                                  const int32_t* __restrict__ offsets, int E,
-                                                                 int fixed_rows, int N, int K, int n_tiles) {
+                                                                 int fixed_rows, int rmin, int rmax, int N, int K,
+                                                                 int n_tiles) {
     using Tl = Tile32<BM, BN, BK, NS, WM, WN>;
     constexpr int NW = Tl::NW, TM = Tl::TM, TN = Tl::TN, WTM = Tl::WTM, WTN = Tl::WTN;
     constexpr int A_BYTES = Tl::A_BYTES, STAGE = Tl::STAGE, LOADS = Tl::LOADS;
     __shared__ __align__(1024) uint8_t smem[NS * STAGE];
 
     int e, rb, re, nt;
-    if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, e, rb, re, nt)) return;
+    if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, rmin, rmax, e, rb, re, nt)) return;
     const int n0 = nt * BN;
     const uint16_t* Be = B + (long)e * strideB;
     const int wave = threadIdx.x / kWave, l = lane_id();

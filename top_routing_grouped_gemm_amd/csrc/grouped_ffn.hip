@@ -24,6 +24,8 @@
 // stage in flight, 16x16x32 bf16 MFMA, fp32 accumulation.
 #include <math.h>
 
+#include <limits.h>
+
 #include "gemm_dma.hpp"
 #include "mfma_tiles.hpp"
 #include "moe_internal.hpp"
@@ -252,17 +254,18 @@ using DmaLarge = DmaCfg<256, 256, 32, 4, 4, 2>;
 using DmaStream = DmaCfg<32, 128, 64, 4, 1, 4>;
 
 // a_kstep / c_cap: see gemm32_kernel (1 / 0 for row-major A / C).
+// [rmin, rmax): the group sizes this launch takes (see xcd_tile).
 template <class C, int EPI>
 hipError_t run_dma(const void* A, long lda, long a_kstep, const int32_t* a_rows, const void* B, long strideB, long ldb,
                    void* Cm, long ldc, long c_cap, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N,
-                   int K, hipStream_t s) {
+                   int K, hipStream_t s, int rmin = 0, int rmax = INT_MAX) {
     const int n_tiles = (N + C::BN - 1) / C::BN;
     // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
     const long grid = max_mtiles(C::BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
                        dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_kstep, a_rows, (const uint16_t*)B,
-                       strideB, ldb, Cm, ldc, c_cap, offsets, E, fixed_rows, N, K, n_tiles);
+                       strideB, ldb, Cm, ldc, c_cap, offsets, E, fixed_rows, rmin, rmax, N, K, n_tiles);
     return hipGetLastError();
 }
 
@@ -291,6 +294,16 @@ hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, lon
                                               max_rows, N, K, s);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
+        case kTileMixed:
+            if (offsets != nullptr && dma_ok<DmaStream>(lda, ldb, N, K) && dma_ok<DmaLarge>(lda, ldb, N, K)) {
+                const hipError_t e = run_dma<DmaStream, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, 0, offsets,
+                                                             E, fixed_rows, max_rows, N, K, s, 0, kStreamRows);
+                if (e != hipSuccess) return e;
+                return run_dma<DmaLarge, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, 0, offsets, E, fixed_rows,
+                                              max_rows, N, K, s, kStreamRows, INT_MAX);
+            }
+            return run_bf16<64, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
+                                                    max_rows, N, K, s);
         case kTileM64:
             return run_bf16<64, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                     max_rows, N, K, s);
@@ -321,6 +334,7 @@ bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt) {
     if (dt != kBF16) return false;
     if (cfg == kTileM128) return dma_ok<DmaLarge>(H, F, F, H);
     if (cfg == kTileM16) return dma_ok<DmaStream>(H, F, F, H);
+    if (cfg == kTileMixed) return dma_ok<DmaLarge>(H, F, F, H) && dma_ok<DmaStream>(H, F, F, H);
     return false;
 }
 
@@ -329,6 +343,13 @@ hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const i
     if (cfg == kTileM128)
         return run_dma<DmaLarge, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, h_cap, offsets, E, 0,
                                               max_rows, F, H, s);
+    if (cfg == kTileMixed) {
+        const hipError_t e = run_dma<DmaStream, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, 0, offsets,
+                                                             E, 0, max_rows, F, H, s, 0, kStreamRows);
+        if (e != hipSuccess) return e;
+        return run_dma<DmaLarge, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, 0, offsets, E, 0,
+                                              max_rows, F, H, s, kStreamRows, INT_MAX);
+    }
     return run_dma<DmaStream, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, 0, offsets, E, 0, max_rows,
                                            F, H, s);
 }
@@ -343,7 +364,7 @@ long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt) {
 TileCfg choose_tile(long rows, int groups) {
     const long mean = groups > 0 ? rows / groups : rows;
     if (mean >= 96) return kTileM128;
-    if (mean >= 24) return kTileM64;
+    if (mean >= 24) return kTileMixed;
     return kTileM16;
 }
 

@@ -14,7 +14,10 @@ constexpr int kDispatchChunk = 256;  // assignments per dispatch workgroup
 constexpr int kSmallAssign = 1024;   // batches up to this many assignments dispatch in one workgroup
 
 // Ragged GEMM tile shapes, chosen on the host from the mean rows per expert.
-enum TileCfg { kTileM16 = 0, kTileM64 = 1, kTileM128 = 2 };
+// kTileMixed: groups of very different sizes (mean 24..95 rows); the weight-
+// streaming shape takes groups under kStreamRows rows, the large shape the rest.
+enum TileCfg { kTileM16 = 0, kTileM64 = 1, kTileM128 = 2, kTileMixed = 3 };
+constexpr int kStreamRows = 32;
 
 inline int dispatch_blocks(long n_assign) { return (int)((n_assign + kDispatchChunk - 1) / kDispatchChunk); }
 
