@@ -32,10 +32,28 @@ __device__ __forceinline__ void combine_store(float4 acc, void* __restrict__ y, 
     }
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm, const int32_t* __restrict__ inv,
-                                                      const float* __restrict__ w, const float4* __restrict__ ysh,
-                                                      int H4, int k, void* __restrict__ y) {
+// Four consecutive y_perm values (group idx = row*H/4 + column/4): fp32, or
+// the 24-bit planes written by the W2 epilogue (upper 16 bits, 8 bytes per
+// group; next 8 bits, 4 bytes per group at lo_off bytes), reassembled exactly.
+template <bool PACKED>
+__device__ __forceinline__ float4 load4(const void* __restrict__ yp, long lo_off, long idx) {
+    if constexpr (PACKED) {
+        const u32x2 h = ((const u32x2*)yp)[idx];
+        const uint32_t l = ((const uint32_t*)((const uint8_t*)yp + lo_off))[idx];
+        return make_float4(__uint_as_float((h[0] << 16) | ((l & 0xffu) << 8)),
+                           __uint_as_float((h[0] & 0xffff0000u) | (((l >> 8) & 0xffu) << 8)),
+                           __uint_as_float((h[1] << 16) | (((l >> 16) & 0xffu) << 8)),
+                           __uint_as_float((h[1] & 0xffff0000u) | ((l >> 24) << 8)));
+    } else {
+        return ((const float4*)yp)[idx];
+    }
+}
+
+template <bool OUT_BF16, bool PACKED>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm, long lo_off,
+                                                      const int32_t* __restrict__ inv, const float* __restrict__ w,
+                                                      const float4* __restrict__ ysh, int H4, int k,
+                                                      void* __restrict__ y) {
     const long t = blockIdx.x;
     for (int c0 = threadIdx.x; c0 < H4; c0 += 512) {
         const int c1 = c0 + 256;
@@ -49,9 +67,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
                 const int j = j0 + u;
                 const int r = j < k ? inv[t * k + j] : -1;
                 ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
-                const float4* row = y_perm + (long)(r >= 0 ? r : 0) * H4;
-                v0[u] = r >= 0 ? row[c0] : make_float4(0.f, 0.f, 0.f, 0.f);
-                v1[u] = (r >= 0 && two) ? row[c1] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const long row = (long)(r >= 0 ? r : 0) * H4;
+                v0[u] = r >= 0 ? load4<PACKED>(y_perm, lo_off, row + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v1[u] = (r >= 0 && two) ? load4<PACKED>(y_perm, lo_off, row + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -86,19 +104,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
     }
 }
 
+template <bool PACKED>
+hipError_t combine(const void* y_perm, long lo_off, const int32_t* inv, const float* w, const float* y_shared, int T,
+                   int H, int k, Dtype out_dt, void* y, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int H4 = H / 4;
+    if (out_dt == kBF16)
+        hipLaunchKernelGGL((combine_kernel<true, PACKED>), dim3(T), dim3(256), 0, s, y_perm, lo_off, inv, w,
+                           (const float4*)y_shared, H4, k, y);
+    else
+        hipLaunchKernelGGL((combine_kernel<false, PACKED>), dim3(T), dim3(256), 0, s, y_perm, lo_off, inv, w,
+                           (const float4*)y_shared, H4, k, y);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared, int T,
                           int H, int k, Dtype out_dt, void* y, hipStream_t s) {
-    if (T == 0) return hipSuccess;
-    const int H4 = H / 4;
-    if (out_dt == kBF16)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, s, (const float4*)y_perm, inv, w,
-                           (const float4*)y_shared, H4, k, y);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, (const float4*)y_perm, inv, w,
-                           (const float4*)y_shared, H4, k, y);
-    return hipGetLastError();
+    return combine<false>(y_perm, 0, inv, w, y_shared, T, H, k, out_dt, y, s);
+}
+
+hipError_t launch_combine_packed(const void* y_planes, long cap, const int32_t* inv, const float* w,
+                                 const float* y_shared, int T, int H, int k, Dtype out_dt, void* y, hipStream_t s) {
+    return combine<true>(y_planes, cap * H * 2, inv, w, y_shared, T, H, k, out_dt, y, s);
 }
 
 }  // namespace moe

@@ -204,9 +204,49 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
 // next GEMM's A-tile loads of 32 k-values over consecutive rows are one
 // contiguous run instead of 64-byte pieces of separate rows. Rows past the
 // group are dropped by an explicit out-of-range offset in that layout.
+//
+// EPI 2 (fp32 result as a 24-bit float): the fp32 bits rounded to their top 24
+// (sign, exponent, 15 mantissa bits; relative error <= 2^-16) go to two planes,
+// the upper 16 bits at C[r*ldc + n] (2-byte elements) and the next 8 bits at
+// byte (C + c_cap*ldc*2)[r*ldc + n], c_cap being the row capacity: 3 bytes per
+// value instead of 4 for a result that is read once more.
 template <int TM, int TN, int WTM, int WTN, int EPI>
 __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, long ldc, long c_cap, int rb, int re,
                                              int n0, int N, int wm, int wn) {
+    if constexpr (EPI == 2) {
+        const int l = lane_id();
+        const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
+            (uint8_t*)C + ((long)rb * ldc + n0) * 2, (short)0, (int)(((long)(re - rb) * ldc - n0) * 2), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
+            (uint8_t*)C + c_cap * ldc * 2 + (long)rb * ldc + n0, (short)0, (int)((long)(re - rb) * ldc - n0),
+            0x00020000);
+        const int c0 = (l & 31) & ~3, m = l & 3;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj) {
+                const int colrel = wn * WTN + jj * 32 + c0;
+                const bool col_ok = n0 + colrel < N;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    float v[4] = {acc[i][jj][4 * p], acc[i][jj][4 * p + 1], acc[i][jj][4 * p + 2],
+                                  acc[i][jj][4 * p + 3]};
+                    quad_transpose(v);
+                    const int rowrel = wm * WTM + i * 32 + 8 * p + 4 * (l >> 5) + m;
+                    const int e = rowrel * (int)ldc + colrel;  // element offset within the tile's rows
+                    uint32_t u[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) u[q] = __float_as_uint(v[q]) + 0x80u;  // round to 24 bits
+                    typedef __attribute__((ext_vector_type(2))) unsigned u2;
+                    const u2 hi = {(u[0] >> 16) | (u[1] & 0xffff0000u), (u[2] >> 16) | (u[3] & 0xffff0000u)};
+                    const uint32_t lo = ((u[0] >> 8) & 0xffu) | (((u[1] >> 8) & 0xffu) << 8) |
+                                        (((u[2] >> 8) & 0xffu) << 16) | (((u[3] >> 8) & 0xffu) << 24);
+                    __builtin_amdgcn_raw_buffer_store_b64(hi, rs_hi, col_ok ? e * 2 : 0x7ffffff0, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(lo, rs_lo, col_ok ? e : 0x7ffffff0, 0, 0);
+                }
+            }
+        return;
+    }
     constexpr int ES = EPI == 0 ? 2 : 4;
     const int l = lane_id();
     const long ldc_b = ldc * ES;

@@ -77,7 +77,7 @@ __device__ __forceinline__ bool locate(const int32_t* __restrict__ offsets, int 
     return find_tile<BM>(offsets, E, mt, e, rb, re);
 }
 
-enum { kEpiSiluOut = 0, kEpiF32Out = 1 };
+enum { kEpiSiluOut = 0, kEpiF32Out = 1, kEpiPacked24 = 2 };
 
 template <int BM, int BN, int BK, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
@@ -359,6 +359,35 @@ long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt) {
     if (!dma_ok<DmaLarge>(H, F, F, H) || !dma_ok<DmaLarge>(F, H, H, F)) return 0;
     if (cap * F * 2 > 0x7fff0000L) return 0;  // 32-bit buffer offsets
     return cap;
+}
+
+bool ffn_down_packs(TileCfg cfg, int F, int H, Dtype dt) {
+    if (dt != kBF16) return false;
+    if (cfg == kTileM128) return dma_ok<DmaLarge>(F, H, H, F);
+    if (cfg == kTileM16) return dma_ok<DmaStream>(F, H, H, F);
+    if (cfg == kTileMixed) return dma_ok<DmaLarge>(F, H, H, F) && dma_ok<DmaStream>(F, H, H, F);
+    return false;
+}
+
+hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, int max_rows, const void* W2, int F,
+                                  int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s) {
+    const long sb = (long)F * H;
+    if (cfg == kTileM128) {
+        if (h_cap > 0)
+            return run_dma<DmaLarge, kEpiPacked24>(h, 32, h_cap, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0,
+                                                   max_rows, H, F, s);
+        return run_dma<DmaLarge, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
+                                               H, F, s);
+    }
+    if (cfg == kTileMixed) {
+        const hipError_t e = run_dma<DmaStream, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets,
+                                                              E, 0, max_rows, H, F, s, 0, kStreamRows);
+        if (e != hipSuccess) return e;
+        return run_dma<DmaLarge, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
+                                               H, F, s, kStreamRows, INT_MAX);
+    }
+    return run_dma<DmaStream, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows, H,
+                                            F, s);
 }
 
 TileCfg choose_tile(long rows, int groups) {

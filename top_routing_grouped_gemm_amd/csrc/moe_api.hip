@@ -113,9 +113,10 @@ int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, in
 }
 
 // row_token != NULL: the W1 launch gathers rows of x through row_token instead of reading x_perm.
+// packed: y_perm is written as the two 24-bit planes of ffn_down_packs (the caller checked that it applies).
 int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* offsets, const void* W1, const void* W2,
                 int T, int H, int F, int E, int k, moe_dtype_t dt, float* y_perm, const void* x, const void* W1s,
-                const void* W2s, int Fs, float* y_shared, void* ws, hipStream_t s) {
+                const void* W2s, int Fs, float* y_shared, void* ws, bool packed, hipStream_t s) {
     const FfnLayout L = ffn_layout(T, F, k, Fs, dt);
     char* base = (char*)ws;
     void* h = base + L.h;
@@ -123,20 +124,20 @@ int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* off
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
     const long hc = moe::h_blocked(cfg, H, F, rows, d);  // h layout shared by the W1 and W2 launches
+    // shared expert: one fixed group of T rows reading x directly
+    void* hs = base + L.h_sh;
+    const moe::TileCfg cs = moe::choose_tile(T, 1);
+    const long hsc = W1s != nullptr ? moe::h_blocked(cs, H, Fs, T, d) : 0;
     if (row_token != nullptr)
         MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, cfg, hc, h, s));
     else
         MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, hc, s));
-    if (W1s != nullptr) {
-        void* hs = base + L.h_sh;
-        const moe::TileCfg cs = moe::choose_tile(T, 1);
-        const long hsc = moe::h_blocked(cs, H, Fs, T, d);
-        MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, hsc, s));
+    if (W1s != nullptr) MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, hsc, s));
+    if (packed)
+        MOE_TRY(moe::launch_ffn_down_packed(h, offsets, E, rows, W2, F, H, cfg, hc, y_perm, rows, s));
+    else
         MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, hc, s));
-        MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, hsc, s));
-    } else {
-        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, hc, s));
-    }
+    if (W1s != nullptr) MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, hsc, s));
     return MOE_OK;
 }
 
@@ -223,7 +224,7 @@ int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const voi
     const int fs = W1s ? Fs : 0;
     if (ws_bytes < ffn_layout(T, F, k, fs, dt).total) return MOE_ERR_WORKSPACE;
     return enqueue_ffn(x_perm, nullptr, expert_offsets, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs, y_shared,
-                       ws, stream);
+                       ws, false, stream);
 }
 
 int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, const float* y_shared, int T, int H,
@@ -266,15 +267,21 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
     void* ffn_ws = base + L.ffn;
     void* route_ws = base + L.route;
 
-    // large row counts: the W1 launch gathers x rows itself and x_perm is never written
-    const bool gather = moe::ffn_up_gathers(moe::choose_tile((long)T * k, E), H, F, (Dtype)dt);
+    // direct-to-LDS shapes: the W1 launch gathers x rows itself (x_perm is never written) and the W2 launch
+    // writes y_perm as 24-bit floats (the combine reads 3 bytes per value instead of 4)
+    const moe::TileCfg cfg = moe::choose_tile((long)T * k, E);
+    const bool gather = moe::ffn_up_gathers(cfg, H, F, (Dtype)dt);
+    const bool packed = moe::ffn_down_packs(cfg, F, H, (Dtype)dt);
     MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, route_ws, stream));
     if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, off, row_token, iv, partial, !gather, stream)) !=
         MOE_OK)
         return st;
     if ((st = enqueue_ffn(x_perm, gather ? row_token : nullptr, off, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs,
-                          y_sh, ffn_ws, stream)) != MOE_OK)
+                          y_sh, ffn_ws, packed, stream)) != MOE_OK)
         return st;
+    if (packed)
+        return hip_status(
+            moe::launch_combine_packed(y_perm, (long)T * k, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
     return hip_status(moe::launch_combine(y_perm, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
 }
 

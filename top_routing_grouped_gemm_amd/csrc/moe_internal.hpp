@@ -48,6 +48,12 @@ hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fix
 // Row capacity for the k-blocked h (the large direct-to-LDS shape with bf16
 // and F % 32 == 0), or 0 for row-major.
 long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt);
+// Whether the W2 launch can write y_perm as a 24-bit float in two planes (the
+// direct-to-LDS shapes): upper 16 bits of each fp32 value at
+// planes[r*H + n] (2 bytes), next 8 bits at ((uint8_t*)planes + cap*H*2)[r*H + n].
+bool ffn_down_packs(TileCfg cfg, int F, int H, Dtype dt);
+hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, int max_rows, const void* W2, int F,
+                                  int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s);
 TileCfg choose_tile(long rows, int groups);
 // Whether the W1 launch for this tile shape can read token rows of x directly
 // through the row -> token map (the permute copy is then not needed).
@@ -55,6 +61,9 @@ bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt);
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
                                 const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s);
 
+// y_perm given as the two planes of ffn_down_packs (cap = row capacity).
+hipError_t launch_combine_packed(const void* y_planes, long cap, const int32_t* inv, const float* w,
+                                 const float* y_shared, int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared,
                           int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
 
