@@ -8,6 +8,12 @@ from .moe_oracle import (  # noqa: F401
     router_logits,
     select_topk,
     route,
+    selection_weights,
+    capacity_slots,
+    capacity_feasible,
+    select_capacity,
+    route_capacity,
+    capacity_gaps,
     dispatch,
     silu,
     expert_ffn,

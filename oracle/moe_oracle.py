@@ -12,6 +12,9 @@ Sources (pages are cited by title/address and section):
      weight under the 0.05 threshold and renormalise), the expert layer (every
      expert is an independent two-layer FFN) and the fusion layer (the output
      is the gate-weighted sum of the chosen experts' outputs).
+     Section 3.2, second routing pitfall: a per-expert selection capacity of
+     tokens*k/experts*1.2; over-capacity experts get -inf and the token
+     chooses again (the capacity-limited routing variant).
 [P3] "跟随一个Token走完路由、分发、专家计算到合并和多机放置的整条路径"
      (m.lsln.cn/news/228042):
      - section "MoE层的结构与token路由" (MoE layer structure and token
@@ -44,7 +47,10 @@ the design notes of the repository):
   each token's experts by id, not by weight);
 * row order inside an expert: ascending token id (a stable counting sort);
 * expert FFN: ``silu(x @ W1[e]) @ W2[e]``, silu(u) = u / (1 + exp(-u)), no
-  biases; shared expert: the same form with weight 1.
+  biases; shared expert: the same form with weight 1;
+* capacity-limited routing: capacity = ceil(T*k/E*factor); tokens choose in
+  ascending id among experts not yet full (serial priority by token id);
+  capacity counts selections, before any drop.
 
 Every function here is pinned by the CPU tests (worked example, drop case,
 library special cases, dense brute force, invariants); none is unpinned.
@@ -52,8 +58,10 @@ library special cases, dense brute force, invariants); none is unpinned.
 from __future__ import annotations
 
 import dataclasses
+import math
 import time
 from typing import Callable, Optional, Sequence, Union
+
 
 import numpy as np
 
@@ -132,16 +140,103 @@ def route(x, Wr, b, k: int, drop_thresh: float = 0.0) -> RouteResult:
     """
     logits = router_logits(x, Wr, b)
     ids, gap = select_topk(logits, k)
-    sel = np.take_along_axis(logits, ids, axis=1)
+    w, keep = selection_weights(logits, ids, drop_thresh)
+    return RouteResult(ids=ids.astype(np.int64), w=w, keep=keep, logits=logits, gap=gap)
+
+
+def selection_weights(logits: np.ndarray, ids: np.ndarray, drop_thresh: float = 0.0):
+    """Softmax over each token's selected logits, then the optional drop.
+
+    [P1] section 2.2, routing layer steps 2-3: the selected logits become
+    weights through a softmax; a weight below the threshold is zeroed and the
+    others renormalised (strictly below is dropped; one pass is a fixed point
+    because the survivors only grow).
+    """
+    sel = np.take_along_axis(np.asarray(logits, dtype=np.float64), ids, axis=1)
     m = sel.max(axis=1, keepdims=True)
     p = np.exp(sel - m)
     w = p / p.sum(axis=1, keepdims=True)
     keep = np.ones_like(w, dtype=bool)
     if drop_thresh > 0.0:
-        keep = w >= drop_thresh          # strictly below the threshold is dropped
+        keep = w >= drop_thresh
         w = np.where(keep, w, 0.0)
         w = w / w.sum(axis=1, keepdims=True)
-    return RouteResult(ids=ids.astype(np.int64), w=w, keep=keep, logits=logits, gap=gap)
+    return w, keep
+
+
+# ------------------------------------------------- capacity-limited routing --
+# [P1] section 3.2, second pitfall ("Top-k 选择忽略专家容量"): every expert gets a
+# selection limit capacity = tokens * k / experts * 1.2; an expert chosen more
+# often than that has its logit set to -inf for the excess tokens, which then
+# choose again. Reading taken here: tokens have priority by ascending id, so
+# token t picks its k best experts among those that the tokens before it have
+# not yet filled (a fixed, deterministic order; ties to the lower id as in
+# plain routing). Capacity counts selections, before any drop.
+
+def capacity_slots(T: int, k: int, E: int, factor: float) -> int:
+    """ceil(T*k/E*factor), evaluated in float64 in that order."""
+    return int(math.ceil(T * k / E * float(factor)))
+
+
+def capacity_feasible(T: int, k: int, E: int, cap: int) -> bool:
+    """A sufficient condition for every token to find k experts with room,
+    checkable before routing: at most floor(T*k/cap) experts can ever be full,
+    so at least E minus that many always have room."""
+    return cap >= 1 and E - (T * k) // cap >= k
+
+
+def select_capacity(logits: np.ndarray, k: int, cap: int) -> np.ndarray:
+    """Capacity-limited top-k: ids [T,k] ascending per row.
+
+    Tokens in ascending id; each takes the k largest logits among experts
+    whose selection count is still below cap (full experts are treated as
+    -inf); ties go to the lower expert id. The comparisons are made on the
+    logits exactly as given (pass float32 values to decide in float32).
+    """
+    T, E = logits.shape
+    count = np.zeros(E, dtype=np.int64)
+    ids = np.zeros((T, k), dtype=np.int64)
+    eid = np.arange(E)
+    for t in range(T):
+        room = count < cap
+        if room.sum() < k:
+            raise ValueError(f"token {t}: fewer than k experts have room")
+        cand = eid[room]
+        vals = logits[t, room]
+        order = np.lexsort((cand, -vals.astype(np.float64)))  # logit descending, then id ascending
+        chosen = np.sort(cand[order[:k]])
+        ids[t] = chosen
+        count[chosen] += 1
+    return ids
+
+
+def route_capacity(x, Wr, b, k: int, drop_thresh: float, factor: float) -> RouteResult:
+    """Capacity-limited routing: fp64 logits, select_capacity, softmax over the
+    selected logits, optional drop. gap = per token, its k-th minus (k+1)-th
+    largest logit among the experts that had room when it chose."""
+    logits = router_logits(x, Wr, b)
+    T, E = logits.shape
+    cap = capacity_slots(T, k, E, factor)
+    ids = select_capacity(logits, k, cap)
+    w, keep = selection_weights(logits, ids, drop_thresh)
+    return RouteResult(ids=ids, w=w, keep=keep, logits=logits, gap=capacity_gaps(logits, ids, cap))
+
+
+def capacity_gaps(logits: np.ndarray, ids: np.ndarray, cap: int) -> np.ndarray:
+    """For each token: smallest selected logit minus largest unselected logit
+    among the experts that still had room when the token chose (inf if none)."""
+    T, E = logits.shape
+    count = np.zeros(E, dtype=np.int64)
+    gap = np.full(T, np.inf)
+    for t in range(T):
+        room = count < cap
+        sel = np.zeros(E, dtype=bool)
+        sel[ids[t]] = True
+        other = room & ~sel
+        if other.any():
+            gap[t] = logits[t, ids[t]].min() - logits[t, other].max()
+        count[ids[t]] += 1
+    return gap
 
 
 def dispatch(ids: np.ndarray, keep: np.ndarray, E: int) -> DispatchResult:
