@@ -116,6 +116,45 @@ int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, in
               size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_route_capacity - router logits, then capacity-limited top-k, softmax
+ * weights and optional drop.
+ *
+ * Page 1 ("MoE大模型的智能调度…", www.jsqmd.com/news/1091713), section 3.2,
+ * second routing pitfall: each expert accepts at most
+ * capacity = tokens * k / experts * 1.2 selections; an over-capacity expert's
+ * logit is set to -inf for the excess tokens, which choose again.
+ *
+ *   cap = ceil(T * k / E * cap_factor)   (double precision, in that order)
+ *   tokens in ascending id each take the k largest logits among experts
+ *   selected fewer than cap times by the tokens before them (ties to the
+ *   lower id); weights and drop as in moe_route, over the final selection.
+ *   Capacity counts selections, before the drop.
+ *
+ * Same x, Wr, bias, outputs and slot order as moe_route; the result is
+ * deterministic. Needs bf16 inputs, E % 8 == 0, E <= 256, H % 64 == 0
+ * (otherwise MOE_ERR_UNSUPPORTED). cap_factor in (0, 1e6]
+ * (MOE_ERR_INVALID_ARG otherwise); MOE_ERR_UNSUPPORTED when
+ * E - floor(T*k/cap) < k, i.e. some token could find fewer than k experts
+ * with room. ws: moe_route_capacity_workspace_bytes(T,H,E,dt) bytes.
+ */
+size_t moe_route_capacity_workspace_bytes(int T, int H, int E, moe_dtype_t dt);
+int moe_route_capacity(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
+                       float drop_thresh, float cap_factor, moe_dtype_t dt, int32_t* topk_ids,
+                       float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_select_capacity - the capacity-limited selection, weights and drop of
+ * moe_route_capacity on given fp32 logits [T,E] (row-major, device), with
+ * the capacity cap given in selections (cap >= 1). Decisions compare the
+ * logits exactly as given. Same outputs as moe_route. MOE_ERR_UNSUPPORTED
+ * when E - floor(T*k/cap) < k. ws: moe_select_capacity_workspace_bytes(T,E).
+ */
+size_t moe_select_capacity_workspace_bytes(int T, int E);
+int moe_select_capacity(const float* logits, int T, int E, int k, float drop_thresh, int cap,
+                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
  * moe_permute - dispatch: group the kept assignments by expert.
  *
  * Page 3, section "一个批次如何变成各专家专属的矩阵": each assignment carries a

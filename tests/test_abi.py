@@ -93,6 +93,45 @@ def test_route_rejects(lib):
     assert lib.moe_route_workspace_bytes(32, 2048, 128, 0) == 0     # fp32 router never splits
 
 
+def test_capacity_rejects(lib):
+    N = None
+    bf16 = 1
+    # workspace queries: router shapes only (bf16, E % 8 == 0, E <= 256, H % 64 == 0)
+    assert lib.moe_route_capacity_workspace_bytes(8192, 2048, 128, bf16) > 8192 * 128 * 4
+    assert lib.moe_route_capacity_workspace_bytes(64, 64, 4, 0) == 0          # fp32: unsupported
+    assert lib.moe_route_capacity_workspace_bytes(64, 96, 8, bf16) == 0       # H % 64 != 0
+    assert lib.moe_select_capacity_workspace_bytes(100, 16) > 0
+    assert lib.moe_select_capacity_workspace_bytes(100, 2000) == 0
+
+    def route(**kw):
+        a = dict(x=_p(), Wr=_p(), b=N, T=2048, H=5120, E=64, k=2, drop=0.0, f=1.2, dt=bf16, ids=_p(), w=_p(),
+                 ws=N, wsb=0, s=N)
+        a.update(kw)
+        return lib.moe_route_capacity(a["x"], a["Wr"], a["b"], a["T"], a["H"], a["E"], a["k"], a["drop"], a["f"],
+                                      a["dt"], a["ids"], a["w"], a["ws"], a["wsb"], a["s"])
+
+    assert route(f=0.0) == moe.MOE_ERR_INVALID_ARG
+    assert route(f=float("nan")) == moe.MOE_ERR_INVALID_ARG
+    assert route(f=float("inf")) == moe.MOE_ERR_INVALID_ARG
+    assert route(f=0.5) == moe.MOE_ERR_UNSUPPORTED        # cap 32: 64 experts could all fill, none left
+    assert route(T=64, H=64, E=4, k=2) == moe.MOE_ERR_UNSUPPORTED   # cap 39: only one expert is sure to have room
+    assert route(dt=0, T=64, H=64, E=64, k=2) == moe.MOE_ERR_UNSUPPORTED   # fp32 router: no logits path
+    assert route() == moe.MOE_ERR_WORKSPACE
+    assert route(ids=N) == moe.MOE_ERR_INVALID_ARG
+
+    def select(**kw):
+        a = dict(lg=_p(), T=100, E=16, k=2, drop=0.0, cap=20, ids=_p(), w=_p(), ws=_p(), wsb=1 << 20, s=N)
+        a.update(kw)
+        return lib.moe_select_capacity(a["lg"], a["T"], a["E"], a["k"], a["drop"], a["cap"], a["ids"], a["w"],
+                                       a["ws"], a["wsb"], a["s"])
+
+    assert select(cap=0) == moe.MOE_ERR_INVALID_ARG
+    assert select(cap=13) == moe.MOE_ERR_UNSUPPORTED      # 16 - 200 // 13 = 1 < 2
+    assert select(wsb=1) == moe.MOE_ERR_WORKSPACE
+    assert select(lg=N) == moe.MOE_ERR_INVALID_ARG
+    assert select(drop=0.7) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_permute_ffn_combine_forward_reject(lib):
     N = None
     # permute: undersized workspace

@@ -23,7 +23,9 @@ from ._binding import (  # noqa: F401
     moe_permute,
     moe_permute_workspace_bytes,
     moe_route,
+    moe_route_capacity,
     moe_route_workspace_bytes,
+    moe_select_capacity,
     moe_workspace_bytes,
     strerror,
     version,

@@ -19,8 +19,9 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_workspace_bytes",
-           "moe_permute_workspace_bytes",
-           "moe_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward")
+           "moe_permute_workspace_bytes", "moe_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
+           "moe_combine", "moe_forward", "moe_route_capacity_workspace_bytes", "moe_route_capacity",
+           "moe_select_capacity_workspace_bytes", "moe_select_capacity")
 
 
 class MoEError(RuntimeError):
@@ -56,6 +57,14 @@ def load_library(path: Optional[str] = None):
     lib.moe_ffn_workspace_bytes.restype = sz
     lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.moe_route.restype = i32
+    lib.moe_route_capacity_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.moe_route_capacity_workspace_bytes.restype = sz
+    lib.moe_route_capacity.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+    lib.moe_route_capacity.restype = i32
+    lib.moe_select_capacity_workspace_bytes.argtypes = [i32, i32]
+    lib.moe_select_capacity_workspace_bytes.restype = sz
+    lib.moe_select_capacity.argtypes = [vp, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+    lib.moe_select_capacity.restype = i32
     lib.moe_permute.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i32
     lib.moe_grouped_ffn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, sz,
@@ -144,6 +153,39 @@ def moe_route(x, Wr, bias, k: int, drop_thresh: float = 0.0, topk_ids=None, topk
                                   _ptr(topk_ids), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream))
     _check(st, "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_route_capacity(x, Wr, bias, k: int, drop_thresh: float = 0.0, cap_factor: float = 1.2, topk_ids=None,
+                       topk_w=None, ws=None, stream=None):
+    """Router logits, capacity-limited top-k, softmax weights (+ drop). Returns (topk_ids, topk_w)."""
+    T, H = x.shape
+    E = Wr.shape[1]
+    dev = x.device
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    dt = _dt(x)
+    ws = _ws(load_library().moe_route_capacity_workspace_bytes(T, H, E, dt), dev) if ws is None else ws
+    st = load_library().moe_route_capacity(_ptr(x), _ptr(Wr), _ptr(bias), T, H, E, k, float(drop_thresh),
+                                           float(cap_factor), dt, _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(),
+                                           _stream(stream))
+    _check(st, "moe_route_capacity")
+    return topk_ids, topk_w
+
+
+def moe_select_capacity(logits, k: int, cap: int, drop_thresh: float = 0.0, topk_ids=None, topk_w=None, ws=None,
+                        stream=None):
+    """Capacity-limited top-k + weights on fp32 logits [T,E]. Returns (topk_ids, topk_w)."""
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    T, E = logits.shape
+    dev = logits.device
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    ws = _ws(load_library().moe_select_capacity_workspace_bytes(T, E), dev) if ws is None else ws
+    st = load_library().moe_select_capacity(_ptr(logits), T, E, k, float(drop_thresh), int(cap), _ptr(topk_ids),
+                                            _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_select_capacity")
     return topk_ids, topk_w
 
 

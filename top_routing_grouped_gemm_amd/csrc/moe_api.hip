@@ -1,5 +1,7 @@
 // C ABI of the MoE-layer forward (declared in include/moe.h): argument
 // checks, workspace layout and the launch sequence on the caller's stream.
+#include <math.h>
+
 #include "moe.h"
 
 #include "moe_internal.hpp"
@@ -197,6 +199,67 @@ int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, in
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
     return hip_status(
         moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, topk_ids, topk_w, ws, stream));
+}
+
+static int capacity_args(int T, int E, int k, int cap) {
+    if (cap < 1) return MOE_ERR_INVALID_ARG;
+    if ((long long)E - ((long long)T * k) / cap < k) return MOE_ERR_UNSUPPORTED;  // some token could lack k experts
+    return MOE_OK;
+}
+
+static size_t route_capacity_layout(int T, int H, int E, size_t* logits_off, size_t* sel_off) {
+    const size_t part = align_up(moe::route_logits_partial_bytes(T, H, E));
+    const size_t lg = align_up((size_t)T * moe::route_logits_ld(E) * sizeof(float));
+    *logits_off = part;
+    *sel_off = part + lg;
+    return part + lg + align_up(moe::capacity_workspace_bytes(T, E));
+}
+
+size_t moe_select_capacity_workspace_bytes(int T, int E) {
+    if (T < 1 || E < 1 || E > kMaxExperts) return 0;
+    return align_up(moe::capacity_workspace_bytes(T, E));
+}
+
+size_t moe_route_capacity_workspace_bytes(int T, int H, int E, moe_dtype_t dt) {
+    if (!valid_dtype(dt) || check_sizes(T, H, 0, E, 1) != MOE_OK) return 0;
+    if (!moe::route_logits_ok(H, E, (Dtype)dt)) return 0;
+    size_t a, b;
+    return route_capacity_layout(T, H, E, &a, &b);
+}
+
+int moe_select_capacity(const float* logits, int T, int E, int k, float drop_thresh, int cap, int32_t* topk_ids,
+                        float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_sizes(T, 8, 0, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if ((st = capacity_args(T, E, k, cap)) != MOE_OK) return st;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (ws == nullptr || ws_bytes < moe_select_capacity_workspace_bytes(T, E)) return MOE_ERR_WORKSPACE;
+    return hip_status(
+        moe::launch_capacity_select(logits, E, T, E, k, cap, drop_thresh, topk_ids, topk_w, ws, stream));
+}
+
+int moe_route_capacity(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
+                       float drop_thresh, float cap_factor, moe_dtype_t dt, int32_t* topk_ids, float* topk_w,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, 0, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if (!(cap_factor > 0.0f) || !(cap_factor <= 1e6f)) return MOE_ERR_INVALID_ARG;  // rejects NaN and inf
+    const double capd = ceil((double)T * k / E * (double)cap_factor);
+    const int cap = capd >= 2147483647.0 ? 2147483647 : (int)capd;
+    if ((st = capacity_args(T, E, k, cap)) != MOE_OK) return st;
+    if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!moe::route_logits_ok(H, E, (Dtype)dt)) return MOE_ERR_UNSUPPORTED;
+    size_t lo, so;
+    const size_t need = route_capacity_layout(T, H, E, &lo, &so);
+    if (ws == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    float* logits = (float*)(base + lo);
+    MOE_TRY(moe::launch_route_logits(x, Wr, bias, T, H, E, logits, base, stream));
+    return hip_status(moe::launch_capacity_select(logits, moe::route_logits_ld(E), T, E, k, cap, drop_thresh,
+                                                  topk_ids, topk_w, base + so, stream));
 }
 
 int moe_permute(const void* x, const int32_t* topk_ids, const float* topk_w, int T, int H, int E, int k,

@@ -23,6 +23,19 @@ inline int dispatch_blocks(long n_assign) { return (int)((n_assign + kDispatchCh
 
 // Router workspace (fp32 partial logits when the H loop is split); 0 when none is needed.
 size_t route_workspace_bytes(int T, int H, int E, Dtype dt);
+// fp32 router logits (x@Wr + bias) to logits[T][route_logits_ld(E)] (bf16
+// inputs, the direct-to-LDS router shapes only); partial holds
+// route_logits_partial_bytes of split sums.
+bool route_logits_ok(int H, int E, Dtype dt);
+int route_logits_ld(int E);
+size_t route_logits_partial_bytes(int T, int H, int E);
+hipError_t launch_route_logits(const void* x, const void* Wr, const float* bias, int T, int H, int E, float* logits,
+                               void* partial, hipStream_t s);
+// Capacity-limited top-k selection on fp32 logits [T][ld] (see capacity.hip).
+constexpr int kCapMaxRounds = 16;
+size_t capacity_workspace_bytes(int T, int E);
+hipError_t launch_capacity_select(const float* logits, int ld, int T, int E, int k, int cap, float drop,
+                                  int32_t* ids, float* w, void* ws, hipStream_t s);
 hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
                         float drop, Dtype dt, int32_t* ids, float* w, void* ws, hipStream_t s);
 

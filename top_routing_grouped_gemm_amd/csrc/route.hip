@@ -18,6 +18,7 @@
 #include "gemm_dma.hpp"
 #include "mfma_tiles.hpp"
 #include "moe_internal.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -27,29 +28,9 @@ constexpr int kRouteBK = 32;
 constexpr int kRouteS = kRouteBK + 8;  // LDS row stride (bf16 elements)
 constexpr int kQMax = 16;              // experts per lane: E <= 1024
 
-// Order-preserving map of a float to an unsigned key (larger float, larger key).
-__device__ __forceinline__ uint32_t ord_key(float v) {
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-
 // Top-k of one token whose E logits sit in LDS at lg[0..E) (E <= 64*Q), one
-// whole wave; lane l holds experts l, l+64, ... (ascending id = q-major order).
-//  1. Radix select: the k-th largest key tau is built bit by bit from the top,
-//     keeping a bit when at least k keys are >= the candidate (a wave ballot
-//     and a popcount per expert slice: no cross-lane shuffles).
-//  2. Keys > tau are selected; keys == tau fill the remaining places in
-//     ascending expert id (ties go to the lower id).
-//  3. Slot = rank of the expert id among the selected (ballot prefix counts).
-//  4. Softmax over the selected logits, optional drop (w < drop -> 0) and
-//     renormalisation; a kept weight is clamped to >= FLT_MIN so that 0.0f
-//     always means dropped.
+// whole wave: radix select, softmax over the selection (+ drop), slots in
+// ascending expert id (topk.hpp).
 template <int Q>
 __device__ void topk_select(const float* lg, int E, int k, float drop, long t, int32_t* __restrict__ ids,
                             float* __restrict__ wout) {
@@ -60,71 +41,13 @@ __device__ void topk_select(const float* lg, int E, int k, float drop, long t, i
     for (int q = 0; q < Q; ++q) {
         const int e = q * kWave + l;
         v[q] = e < E ? lg[e] : -INFINITY;
-        key[q] = e < E ? ord_key(v[q] + 0.0f) : 0u;  // -0 keyed as +0 (equal logits tie); 0 is below every logit
+        key[q] = e < E ? ord_key(v[q] + 0.0f) : 0u;
     }
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        int c = 0;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) c += __popcll(__ballot(key[q] >= cand));
-        if (c >= k) tau = cand;
-    }
-    int n_gt = 0;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) n_gt += __popcll(__ballot(key[q] > tau));
-    const int need = k - n_gt;  // >= 1 places left for keys equal to tau
-    const unsigned long long below = (1ull << l) - 1ull;
-    bool sel[Q];
-    int ties = 0;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const unsigned long long m = __ballot(key[q] == tau);
-        const int before = ties + __popcll(m & below);
-        sel[q] = key[q] > tau || (key[q] == tau && before < need);
-        ties += __popcll(m);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-        if (sel[q]) mx = fmaxf(mx, v[q]);
-    mx = wave_max(mx);
-    float p[Q], ps = 0.0f;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        p[q] = sel[q] ? expf(v[q] - mx) : 0.0f;
-        ps += p[q];
-    }
-    const float sum = wave_sum(ps);
-    bool kept[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        p[q] = p[q] / sum;
-        kept[q] = sel[q];
-    }
-    if (drop > 0.0f) {
-        float ks = 0.0f;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            kept[q] = sel[q] && !(p[q] < drop);
-            if (!kept[q]) p[q] = 0.0f;
-            ks += p[q];
-        }
-        const float kept_sum = wave_sum(ks);
-#pragma unroll
-        for (int q = 0; q < Q; ++q) p[q] = p[q] / kept_sum;
-    }
-    int base = 0;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const unsigned long long m = __ballot(sel[q]);
-        if (sel[q]) {
-            const int slot = base + __popcll(m & below);
-            ids[t * k + slot] = q * kWave + l;
-            wout[t * k + slot] = kept[q] ? fmaxf(p[q], FLT_MIN) : 0.0f;
-        }
-        base += __popcll(m);
-    }
+    bool sel[Q], kept[Q];
+    float p[Q];
+    radix_select<Q>(key, k, sel);
+    softmax_drop<Q>(v, sel, drop, p, kept);
+    write_slots<Q>(sel, kept, p, t, k, ids, wout);
 }
 
 __device__ void topk_one_token(const float* lg, int E, int k, float drop, long t, int32_t* __restrict__ ids,
@@ -586,7 +509,58 @@ hipError_t launch_bf16(const uint16_t* x, const uint16_t* Wr, const float* bias,
     return hipGetLastError();
 }
 
+// logits[t*EP + e] = sum over the S partial rows (in split order) + bias[e]
+// for e < E, 0 for the padding columns (capacity-limited selection input).
+__global__ __launch_bounds__(256) void logits_sum_kernel(const float* __restrict__ partial, int S, int T, int EP,
+                                                         const float* __restrict__ bias, int E,
+                                                         float* __restrict__ logits) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    const long n = (long)T * EP;
+    if (i >= n) return;
+    const int e = (int)(i % EP);
+    float v = 0.0f;
+    for (int sp = 0; sp < S; ++sp) v += partial[sp * n + i];
+    logits[i] = e < E ? v + (bias != nullptr ? bias[e] : 0.0f) : 0.0f;
+}
+
+template <int EP>
+hipError_t launch_logits(const uint16_t* x, const uint16_t* Wr, const float* bias, int T, int H, int E,
+                         float* logits, float* partial, hipStream_t s) {
+    const int S = route_splits(T, H);
+    const int steps = H / kR2BK / S;
+    const dim3 grid((T + kR2Rows - 1) / kR2Rows, S);
+    hipLaunchKernelGGL((route_v2_kernel<EP, true>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, 1, 0.0f, steps,
+                       (int32_t*)nullptr, (float*)nullptr, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long n = (long)T * EP;
+    hipLaunchKernelGGL(logits_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)partial, S,
+                       T, EP, bias, E, logits);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool route_logits_ok(int H, int E, Dtype dt) { return dt == kBF16 && route_v2_ok(H, E); }
+
+int route_logits_ld(int E) { return route_ep(E); }
+
+size_t route_logits_partial_bytes(int T, int H, int E) {
+    return (size_t)route_splits(T, H) * T * route_ep(E) * sizeof(float);
+}
+
+hipError_t launch_route_logits(const void* x, const void* Wr, const float* bias, int T, int H, int E, float* logits,
+                               void* partial, hipStream_t s) {
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* wb = (const uint16_t*)Wr;
+    float* part = (float*)partial;
+    switch (route_ep(E)) {
+        case 32: return launch_logits<32>(xb, wb, bias, T, H, E, logits, part, s);
+        case 64: return launch_logits<64>(xb, wb, bias, T, H, E, logits, part, s);
+        case 128: return launch_logits<128>(xb, wb, bias, T, H, E, logits, part, s);
+        default: return launch_logits<256>(xb, wb, bias, T, H, E, logits, part, s);
+    }
+}
 
 size_t route_workspace_bytes(int T, int H, int E, Dtype dt) {
     if (dt != kBF16 || !route_v2_ok(H, E)) return 0;
