@@ -176,6 +176,43 @@ def measured_traffic(key):
     return None
 
 
+def capacity_times(name, factor, reps=50):
+    """Capacity-limited routing next to plain routing on one workload: HIP-event times of moe_route and
+    moe_route_capacity (router logits + capacity selection), the capacity, and the largest expert before/after."""
+    import numpy as np
+    import torch
+
+    import gen
+    import top_routing_grouped_gemm_amd as moe
+
+    dev = torch.device("cuda:0")
+    I = gen.make_inputs(name)
+    d = gen.to_device(I, dev)
+    s = torch.cuda.current_stream()
+    T, H, E, k = I.T, I.H, I.E, I.k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lib = moe.load_library()
+    rws = torch.empty(max(moe.moe_route_workspace_bytes(T, H, E, d["x"].dtype), 1), dtype=torch.uint8, device=dev)
+    cws = torch.empty(lib.moe_route_capacity_workspace_bytes(T, H, E, moe.MOE_BF16), dtype=torch.uint8, device=dev)
+
+    def plain():
+        moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop, topk_ids=ids, topk_w=w, ws=rws)
+
+    def capped():
+        moe.moe_route_capacity(d["x"], d["Wr"], d["bias"], k, I.drop, factor, topk_ids=ids, topk_w=w, ws=cws)
+
+    plain()
+    torch.cuda.synchronize()
+    before = int(torch.bincount(ids.flatten().long(), minlength=E).max())
+    t_plain = event_time_ms(plain, reps, s)
+    t_cap = event_time_ms(capped, reps, s)
+    after = int(torch.bincount(ids.flatten().long(), minlength=E).max())
+    cap = int(np.ceil(T * k / E * np.float64(np.float32(factor))))
+    return {"workload": name, "capacity_factor": factor, "capacity": cap, "route_ms": round(t_plain, 5),
+            "route_capacity_ms": round(t_cap, 5), "max_rows_per_expert": {"plain": before, "capped": after}}
+
+
 def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
     """The fp64 oracle, as it stands, on the host cores: whole prefill batches, repeated until about 10 s."""
     import numpy as np
@@ -216,6 +253,8 @@ def main():
                     help="time one workload only (profiling runs and the per-workload table); prints its stage times")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="with --only: time capacity-limited routing (this factor) against plain routing")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -237,6 +276,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return
+    if args.only and args.capacity_factor > 0:
+        print(json.dumps(capacity_times(args.only, args.capacity_factor)), flush=True)
         return
     if args.only:
         _, res = run_workload(args.only, args.steps, args.warmup, args.stage_reps)

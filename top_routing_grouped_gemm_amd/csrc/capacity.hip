@@ -30,7 +30,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kCapChunk = 64;  // tokens per workgroup in a round (4 waves x 16)
+constexpr int kCapThreads = 1024;                // 16 waves per round workgroup
+constexpr int kCapWaves = kCapThreads / kWave;
+constexpr int kCapTPW = 4;                       // tokens per wave, logit rows loaded up front
+constexpr int kCapChunk = kCapWaves * kCapTPW;   // 64 tokens per workgroup
+static_assert(kCapChunk == kWave, "the holder search gives one lane per token of a chunk");
 constexpr int kCapMaxE = 1024;
 enum { kDone = 0, kCounter = 1, kRounds = 2 };
 
@@ -73,70 +77,120 @@ __device__ __forceinline__ void token_keys(const float* __restrict__ row, int E,
 }
 
 template <int Q>
-__global__ __launch_bounds__(256) void cap_round_kernel(const float* __restrict__ logits, int ld, int T, int E, int k,
-                                                        int cap, int* __restrict__ tau, int* __restrict__ ctl,
-                                                        int* __restrict__ hist, int32_t* __restrict__ ids,
-                                                        int nchunks) {
+__global__ __launch_bounds__(kCapThreads) void cap_round_kernel(const float* __restrict__ logits, int ld, int T, int E,
+                                                                int k, int cap, int* __restrict__ tau,
+                                                                int* __restrict__ ctl, int* __restrict__ hist,
+                                                                int32_t* __restrict__ ids, int nchunks) {
     __shared__ int tau_s[kCapMaxE];
-    __shared__ int h[kCapMaxE];
+    __shared__ int h[kCapMaxE];    // chunk histogram, then per-group sums [G][E]
+    __shared__ int cross[kCapMaxE];  // chunk * 64 + rank - 1 of the cap-th holder, or -1
     __shared__ int last, changed;
     if (__hip_atomic_load(&ctl[kDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;  // converged
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
-    for (int e = tid; e < E; e += 256) {
+    const long t0 = (long)blockIdx.x * kCapChunk + wave * kCapTPW;
+    float v[kCapTPW][Q];  // this wave's token rows, all loads issued before any selection
+#pragma unroll
+    for (int i = 0; i < kCapTPW; ++i)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int e = q * kWave + l;
+            v[i][q] = (t0 + i < T && e < E) ? logits[(t0 + i) * ld + e] : -INFINITY;
+        }
+    for (int e = tid; e < E; e += kCapThreads) {
         tau_s[e] = tau[e];
         h[e] = 0;
     }
     if (tid == 0) changed = 0;
     __syncthreads();
-    const long t0 = (long)blockIdx.x * kCapChunk + wave * (kCapChunk / 4);
-    for (int i = 0; i < kCapChunk / 4; ++i) {
+#pragma unroll
+    for (int i = 0; i < kCapTPW; ++i) {
         const long t = t0 + i;
         if (t >= T) break;  // wave-uniform
-        float v[Q];
         uint32_t key[Q];
         bool sel[Q], kept[Q];
         float p[Q];
-        token_keys<Q>(logits + t * ld, E, t, tau_s, v, key);
-        radix_select<Q>(key, k, sel);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            kept[q] = sel[q];
+            const int e = q * kWave + l;
+            key[q] = (e < E && t < tau_s[e]) ? ord_key(v[i][q] + 0.0f) : 0u;
+            kept[q] = false;
             p[q] = 0.0f;
         }
+        radix_select<Q>(key, k, sel);
         write_slots<Q>(sel, kept, p, t, k, ids, nullptr);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if (sel[q]) atomicAdd(&h[q * kWave + l], 1);  // order-free: only a count
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 256) hist[(long)blockIdx.x * E + e] = h[e];
-    __threadfence();  // release this workgroup's ids and histogram device-wide
+    for (int e = tid; e < E; e += kCapThreads) hist[(long)blockIdx.x * E + e] = h[e];
+    // The barrier completes every wave's stores of this workgroup; one thread's
+    // device-scope fences then act on the shared caches for all of them: the
+    // release writes this XCD's L2 back so the other XCDs see the ids and the
+    // histogram, the acquire in the last workgroup drops stale cached lines
+    // before it reads everybody's results.
     __syncthreads();
-    if (tid == 0)
+    if (tid == 0) {
+        __threadfence();
         last = __hip_atomic_fetch_add(&ctl[kCounter], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == nchunks - 1;
+        if (last) __threadfence();
+    }
     __syncthreads();
     if (!last) return;
-    __threadfence();  // acquire every workgroup's ids and histogram
-    // last workgroup: tau[e] = one past the token holding e's cap-th selection
-    for (int e = tid; e < E; e += 256) {
-        int before = 0, c = 0;
-        for (; c < nchunks; ++c) {
-            const int hc = hist[(long)c * E + e];
-            if (before + hc >= cap) break;
-            before += hc;
+
+    // Last workgroup. (1) Where does expert e's count reach cap? G groups of E
+    // threads each sum a contiguous range of chunks (16 loads in flight), the
+    // group whose range holds the crossing finds the chunk and the rank there.
+    const int G = kCapThreads / E > 0 ? kCapThreads / E : 1;
+    const int per = (nchunks + G - 1) / G;
+    const int g = tid / E, e = tid % E;
+    const bool act = g < G && tid < G * E;
+    const int c_lo = g * per, c_hi = min(nchunks, c_lo + per);
+    int gs = 0;
+    if (act) {
+        for (int c0 = c_lo; c0 < c_hi; c0 += 16) {
+            int hc[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) hc[u] = c0 + u < c_hi ? hist[(long)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) gs += hc[u];
         }
-        if (c == nchunks) continue;  // fewer than cap holders: available to every token
-        int r = cap - before;        // 1-based rank of the cap-th holder inside chunk c
-        int tnew = T;
-        const long te = min((long)T, (long)(c + 1) * kCapChunk);
-        for (long t = (long)c * kCapChunk; t < te && tnew == T; ++t)
-            for (int j = 0; j < k; ++j)
-                if (ids[t * k + j] == e && --r == 0) {
-                    tnew = (int)t + 1;
+    }
+    __syncthreads();  // h becomes the [G][E] group sums
+    if (act) h[g * E + e] = gs;
+    for (int x = tid; x < E; x += kCapThreads) cross[x] = -1;
+    __syncthreads();
+    if (act) {
+        int base = 0;
+        for (int i = 0; i < g; ++i) base += h[i * E + e];
+        if (base < cap && base + gs >= cap) {  // the cap-th holder is in this group's range
+            int run = base;
+            for (int c = c_lo; c < c_hi; ++c) {
+                const int hc = hist[(long)c * E + e];
+                if (run + hc >= cap) {
+                    cross[e] = c * kCapChunk + (cap - run) - 1;
                     break;
                 }
-        if (tnew < tau_s[e]) {
-            tau[e] = tnew;
+                run += hc;
+            }
+        }
+    }
+    __syncthreads();
+    // (2) The holder itself: one wave per crossing expert, lane i tests token
+    // chunk*64 + i; the (rank)-th set bit of the ballot, in token order.
+    for (int x = wave; x < E; x += kCapWaves) {
+        const int cr = cross[x];
+        if (cr < 0) continue;  // wave-uniform (LDS value)
+        const int c = cr / kCapChunk, rank = cr % kCapChunk;  // rank: 0-based
+        const long t = (long)c * kCapChunk + l;
+        bool has = false;
+        if (t < T)
+            for (int j = 0; j < k; ++j) has = has || ids[t * k + j] == x;
+        unsigned long long m = __ballot(has);
+        for (int i = 0; i < rank; ++i) m &= m - 1;  // drop the lowest set bits before the wanted one
+        const int tnew = c * kCapChunk + __ffsll((long long)m) - 1 + 1;
+        if (l == 0 && tnew < tau_s[x]) {
+            tau[x] = tnew;
             atomicOr(&changed, 1);
         }
     }
@@ -217,8 +271,8 @@ hipError_t run_capacity(const float* logits, int ld, int T, int E, int k, int ca
     const int nchunks = cap_chunks(T);
     hipLaunchKernelGGL(cap_init_kernel, dim3((E + 255) / 256), dim3(256), 0, s, c.tau, c.ctl, E, T);
     for (int r = 0; r < kCapMaxRounds; ++r)
-        hipLaunchKernelGGL((cap_round_kernel<Q>), dim3(nchunks), dim3(256), 0, s, logits, ld, T, E, k, cap, c.tau,
-                           c.ctl, c.hist, ids, nchunks);
+        hipLaunchKernelGGL((cap_round_kernel<Q>), dim3(nchunks), dim3(kCapThreads), 0, s, logits, ld, T, E, k, cap,
+                           c.tau, c.ctl, c.hist, ids, nchunks);
     hipLaunchKernelGGL((cap_serial_kernel<Q>), dim3(1), dim3(64), 0, s, logits, ld, T, E, k, cap,
                        (const int*)c.ctl, ids);
     hipLaunchKernelGGL((cap_weights_kernel<Q>), dim3((T + 3) / 4), dim3(256), 0, s, logits, ld, T, E, k, drop, ids,
