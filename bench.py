@@ -213,6 +213,54 @@ def capacity_times(name, factor, reps=50):
             "route_capacity_ms": round(t_cap, 5), "max_rows_per_expert": {"plain": before, "capped": after}}
 
 
+def padded_times(name, reps=10):
+    """Ablation: the padded fixed-shape layout (every expert padded to the largest count C) against the ragged
+    grouped FFN on one workload. HIP-event times of dispatch, grouped FFN and combine for both, and the padded
+    work relative to the ragged work (E*C rows against A)."""
+    import torch
+
+    import gen
+    import top_routing_grouped_gemm_amd as moe
+
+    dev = torch.device("cuda:0")
+    I = gen.make_inputs(name)
+    d = gen.to_device(I, dev)
+    s = torch.cuda.current_stream()
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], I.k, I.drop)
+    x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, I.E)
+    torch.cuda.synchronize()
+    counts = (off[1:] - off[:-1]).cpu()
+    A, C = int(counts.sum()), int(counts.max())
+    E, T, k, H = I.E, I.T, I.k, I.H
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    fws = torch.empty(moe.moe_ffn_workspace_bytes(T, I.F, E, k, 0, d["x"].dtype), dtype=torch.uint8, device=dev)
+    x_pad = torch.empty((E * C, H), dtype=d["x"].dtype, device=dev)
+    inv_pad = torch.empty((T, k), dtype=torch.int32, device=dev)
+    y_pad = torch.empty((E * C, H), dtype=torch.float32, device=dev)
+    pws = torch.empty(moe.load_library().moe_grouped_ffn_padded_workspace_bytes(E, C, H, I.F, moe.MOE_BF16),
+                      dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    rag = {
+        "dispatch": event_time_ms(lambda: moe.moe_permute(d["x"], ids, w, E, x_perm=x_perm, expert_offsets=off,
+                                                          row_token=row_token, inv=inv), reps, s),
+        "grouped_ffn": event_time_ms(lambda: moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm,
+                                                                 ws=fws), reps, s),
+        "combine": event_time_ms(lambda: moe.moe_combine(y_perm, inv, w, y=y), reps, s),
+    }
+    pad = {
+        "dispatch": event_time_ms(lambda: moe.moe_pad_dispatch(d["x"], ids, off, row_token, inv, E, C, x_pad=x_pad,
+                                                               inv_pad=inv_pad), reps, s),
+        "grouped_ffn": event_time_ms(lambda: moe.moe_grouped_ffn_padded(x_pad, d["W1"], d["W2"], C, y_pad=y_pad,
+                                                                        ws=pws), reps, s),
+        "combine": event_time_ms(lambda: moe.moe_combine(y_pad, inv_pad, w, y=y), reps, s),
+    }
+    return {"workload": name, "rows_ragged": A, "experts": E, "pad_rows_per_expert": C, "rows_padded": E * C,
+            "padding_flop_ratio": round(E * C / A, 3),
+            "ragged_ms": {k_: round(v, 5) for k_, v in rag.items()},
+            "padded_ms": {k_: round(v, 5) for k_, v in pad.items()},
+            "grouped_ffn_speedup_of_ragged": round(pad["grouped_ffn"] / rag["grouped_ffn"], 3)}
+
+
 def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
     """The fp64 oracle, as it stands, on the host cores: whole prefill batches, repeated until about 10 s."""
     import numpy as np
@@ -255,6 +303,8 @@ def main():
                     help="run only a plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="with --only: time capacity-limited routing (this factor) against plain routing")
+    ap.add_argument("--padded", action="store_true",
+                    help="with --only: time the padded fixed-shape layout against the ragged grouped FFN")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -276,6 +326,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return
+    if args.only and args.padded:
+        print(json.dumps(padded_times(args.only)), flush=True)
         return
     if args.only and args.capacity_factor > 0:
         print(json.dumps(capacity_times(args.only, args.capacity_factor)), flush=True)

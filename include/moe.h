@@ -155,6 +155,31 @@ int moe_select_capacity(const float* logits, int T, int E, int k, float drop_thr
                         hipStream_t stream);
 
 /*
+ * Padded fixed-shape layout - the alternative to the ragged grouped GEMM,
+ * kept as an ablation that measures what the ragged scheduler saves.
+ *
+ * Page 3, section "单机MoE执行流水线": experts receive different row counts;
+ * they can be padded to one shape for a fixed batched GEMM, or run ragged in
+ * one grouped kernel (the path above).
+ *
+ * moe_pad_dispatch: from moe_permute's outputs, x_pad [E*C, H] dt with
+ *   x_pad[e*C + i] = x[row_token[expert_offsets[e] + i]] for i < count_e,
+ *   zero rows for count_e <= i < C; inv_pad [T*k]: e*C + i for a kept slot
+ *   with i = its row inside expert e, -1 if dropped or i >= C (a capacity C
+ *   below the largest count drops those rows). topk_ids as from moe_route.
+ * moe_grouped_ffn_padded: y_pad [E*C, H] fp32 = every expert's FFN over its
+ *   C rows (the grouped kernels with E uniform groups). moe_combine then
+ *   takes (y_pad, inv_pad) in place of (y_perm, inv).
+ * ws: moe_grouped_ffn_padded_workspace_bytes(E,C,H,F,dt) bytes.
+ */
+int moe_pad_dispatch(const void* x, const int32_t* topk_ids, const int32_t* expert_offsets,
+                     const int32_t* row_token, const int32_t* inv, int T, int H, int E, int k, int C,
+                     moe_dtype_t dt, void* x_pad, int32_t* inv_pad, hipStream_t stream);
+size_t moe_grouped_ffn_padded_workspace_bytes(int E, int C, int H, int F, moe_dtype_t dt);
+int moe_grouped_ffn_padded(const void* x_pad, const void* W1, const void* W2, int E, int C, int H, int F,
+                           moe_dtype_t dt, float* y_pad, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * moe_permute - dispatch: group the kept assignments by expert.
  *
  * Page 3, section "一个批次如何变成各专家专属的矩阵": each assignment carries a

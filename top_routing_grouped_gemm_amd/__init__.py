@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     moe_ffn_workspace_bytes,
     moe_forward,
     moe_grouped_ffn,
+    moe_grouped_ffn_padded,
+    moe_pad_dispatch,
     moe_permute,
     moe_permute_workspace_bytes,
     moe_route,

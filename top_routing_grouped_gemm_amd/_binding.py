@@ -21,7 +21,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_workspace_bytes",
            "moe_permute_workspace_bytes", "moe_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_forward", "moe_route_capacity_workspace_bytes", "moe_route_capacity",
-           "moe_select_capacity_workspace_bytes", "moe_select_capacity")
+           "moe_select_capacity_workspace_bytes", "moe_select_capacity", "moe_pad_dispatch",
+           "moe_grouped_ffn_padded_workspace_bytes", "moe_grouped_ffn_padded")
 
 
 class MoEError(RuntimeError):
@@ -65,6 +66,12 @@ def load_library(path: Optional[str] = None):
     lib.moe_select_capacity_workspace_bytes.restype = sz
     lib.moe_select_capacity.argtypes = [vp, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.moe_select_capacity.restype = i32
+    lib.moe_pad_dispatch.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_pad_dispatch.restype = i32
+    lib.moe_grouped_ffn_padded_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.moe_grouped_ffn_padded_workspace_bytes.restype = sz
+    lib.moe_grouped_ffn_padded.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+    lib.moe_grouped_ffn_padded.restype = i32
     lib.moe_permute.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i32
     lib.moe_grouped_ffn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, sz,
@@ -224,6 +231,33 @@ def moe_grouped_ffn(x_perm, expert_offsets, W1, W2, T: int, k: int, y_perm=None,
                                         _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_grouped_ffn")
     return y_perm, y_shared
+
+
+def moe_pad_dispatch(x, topk_ids, expert_offsets, row_token, inv, E: int, C: int, x_pad=None, inv_pad=None,
+                     stream=None):
+    """Padded layout from moe_permute's maps. Returns (x_pad [E*C,H], inv_pad [T,k])."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    x_pad = torch.empty((E * C, H), dtype=x.dtype, device=dev) if x_pad is None else x_pad
+    inv_pad = torch.empty((T, k), dtype=torch.int32, device=dev) if inv_pad is None else inv_pad
+    st = load_library().moe_pad_dispatch(_ptr(x), _ptr(topk_ids), _ptr(expert_offsets), _ptr(row_token), _ptr(inv),
+                                         T, H, E, k, C, _dt(x), _ptr(x_pad), _ptr(inv_pad), _stream(stream))
+    _check(st, "moe_pad_dispatch")
+    return x_pad, inv_pad
+
+
+def moe_grouped_ffn_padded(x_pad, W1, W2, C: int, y_pad=None, ws=None, stream=None):
+    """Every expert's FFN over its C padded rows. Returns y_pad [E*C,H] fp32."""
+    E, H, F = W1.shape
+    dev = x_pad.device
+    y_pad = torch.empty((E * C, H), dtype=torch.float32, device=dev) if y_pad is None else y_pad
+    need = load_library().moe_grouped_ffn_padded_workspace_bytes(E, C, H, F, _dt(x_pad))
+    ws = _ws(need, dev) if ws is None else ws
+    st = load_library().moe_grouped_ffn_padded(_ptr(x_pad), _ptr(W1), _ptr(W2), E, C, H, F, _dt(x_pad), _ptr(y_pad),
+                                               _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_grouped_ffn_padded")
+    return y_pad
 
 
 def moe_combine(y_perm, inv, topk_w, y_shared=None, out_dtype=torch.float32, y=None, stream=None):

@@ -291,3 +291,69 @@ hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32
 }
 
 }  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Padded fixed-shape layout (the ablation of the ragged scheduler): every
+// expert gets exactly C rows. Page 3, section "单机MoE执行流水线": batching
+// experts with different row counts either pads them to one shape or runs a
+// grouped kernel over the ragged groups; this is the padded alternative.
+namespace moe {
+
+namespace {
+
+// x_pad[e*C + i] = x[row_token[offsets[e] + i]] for i < count_e (and i < C),
+// zero for the padding rows. One wave per padded row, 16-byte chunks.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const u32x4* __restrict__ x, const int32_t* __restrict__ row_token,
+                                                       const int32_t* __restrict__ offsets, int C, long rows, int V,
+                                                       u32x4* __restrict__ x_pad) {
+    const long p = (long)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (p >= rows) return;
+    const int e = (int)(p / C), i = (int)(p % C);
+    const int cnt = offsets[e + 1] - offsets[e];
+    const long src = i < cnt ? (long)row_token[offsets[e] + i] * V : -1;
+    for (int c = lane_id(); c < V; c += kWave) x_pad[p * V + c] = src >= 0 ? x[src + c] : u32x4{0u, 0u, 0u, 0u};
+}
+
+// inv_pad[t*k+j] = e*C + (inv - offsets[e]) for a kept slot whose row index
+// inside its expert is < C, else -1 (dropped, or beyond the padded shape).
+__global__ __launch_bounds__(256) void pad_inv_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ inv,
+                                                      const int32_t* __restrict__ offsets, long n, int E, int C,
+                                                      int32_t* __restrict__ inv_pad) {
+    const long a = (long)blockIdx.x * 256 + threadIdx.x;
+    if (a >= n) return;
+    const int r = inv[a], e = ids[a];
+    int out = -1;
+    if (r >= 0 && (unsigned)e < (unsigned)E) {
+        const int i = r - offsets[e];
+        if (i < C) out = e * C + i;
+    }
+    inv_pad[a] = out;
+}
+
+__global__ void uniform_offsets_kernel(int32_t* __restrict__ offsets, int E, int C) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e <= E) offsets[e] = e * C;
+}
+
+}  // namespace
+
+hipError_t launch_pad_dispatch(const void* x, const int32_t* ids, const int32_t* offsets, const int32_t* row_token,
+                               const int32_t* inv, int T, int k, int E, int C, int row_bytes, void* x_pad,
+                               int32_t* inv_pad, hipStream_t s) {
+    const long rows = (long)E * C;
+    const int V = row_bytes / 16;
+    if (rows > 0)
+        hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const u32x4*)x,
+                           row_token, offsets, C, rows, V, (u32x4*)x_pad);
+    const long n = (long)T * k;
+    hipLaunchKernelGGL(pad_inv_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids, inv, offsets, n, E, C,
+                       inv_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_uniform_offsets(int32_t* offsets, int E, int C, hipStream_t s) {
+    hipLaunchKernelGGL(uniform_offsets_kernel, dim3((E + 1 + 255) / 256), dim3(256), 0, s, offsets, E, C);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -201,6 +201,44 @@ int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, in
         moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, topk_ids, topk_w, ws, stream));
 }
 
+size_t moe_grouped_ffn_padded_workspace_bytes(int E, int C, int H, int F, moe_dtype_t dt) {
+    if (!valid_dtype(dt) || E < 1 || E > kMaxExperts || C < 1 || check_sizes(1, H, F, E, 1) != MOE_OK || F < 1)
+        return 0;
+    if ((long long)E * C >= (1LL << 31)) return 0;
+    return align_up((size_t)(E + 1) * sizeof(int32_t)) + ffn_layout(E * C, F, 1, 0, dt).total;
+}
+
+int moe_pad_dispatch(const void* x, const int32_t* topk_ids, const int32_t* expert_offsets, const int32_t* row_token,
+                     const int32_t* inv, int T, int H, int E, int k, int C, moe_dtype_t dt, void* x_pad,
+                     int32_t* inv_pad, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, 0, E, k);
+    if (st != MOE_OK) return st;
+    if (C < 1) return MOE_ERR_INVALID_ARG;
+    if ((long long)E * C >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!x || !topk_ids || !expert_offsets || !row_token || !inv || !x_pad || !inv_pad) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_pad_dispatch(x, topk_ids, expert_offsets, row_token, inv, T, k, E, C,
+                                               (int)(H * elem_bytes(dt)), x_pad, inv_pad, stream));
+}
+
+int moe_grouped_ffn_padded(const void* x_pad, const void* W1, const void* W2, int E, int C, int H, int F,
+                           moe_dtype_t dt, float* y_pad, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    if (E < 1 || C < 1 || H < 1 || F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(1, H, F, E, 1);
+    if (st != MOE_OK) return st;
+    if ((long long)E * C >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!x_pad || !W1 || !W2 || !y_pad) return MOE_ERR_INVALID_ARG;
+    const size_t need = moe_grouped_ffn_padded_workspace_bytes(E, C, H, F, dt);
+    if (ws == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    int32_t* offsets = (int32_t*)ws;
+    void* ffn_ws = (char*)ws + align_up((size_t)(E + 1) * sizeof(int32_t));
+    MOE_TRY(moe::launch_uniform_offsets(offsets, E, C, stream));
+    // the same grouped kernels, over E groups of exactly C rows
+    return enqueue_ffn(x_pad, nullptr, offsets, W1, W2, E * C, H, F, E, 1, dt, y_pad, nullptr, nullptr, nullptr, 0,
+                       nullptr, ffn_ws, false, stream);
+}
+
 static int capacity_args(int T, int E, int k, int cap) {
     if (cap < 1) return MOE_ERR_INVALID_ARG;
     if ((long long)E - ((long long)T * k) / cap < k) return MOE_ERR_UNSUPPORTED;  // some token could lack k experts

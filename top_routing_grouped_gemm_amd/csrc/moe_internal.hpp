@@ -43,6 +43,11 @@ hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T,
 hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial,
                         hipStream_t s);
 hipError_t launch_scan(int32_t* partial, int n_blocks, int E, int32_t* offsets, hipStream_t s);
+// Padded fixed-shape layout (ablation): C rows per expert.
+hipError_t launch_pad_dispatch(const void* x, const int32_t* ids, const int32_t* offsets, const int32_t* row_token,
+                               const int32_t* inv, int T, int k, int E, int C, int row_bytes, void* x_pad,
+                               int32_t* inv_pad, hipStream_t s);
+hipError_t launch_uniform_offsets(int32_t* offsets, int E, int C, hipStream_t s);
 hipError_t launch_dispatch_small(const int32_t* ids, const float* w, int n_assign, int k, int E, int32_t* offsets,
                                  int32_t* row_token, int32_t* inv, hipStream_t s);
 hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* partial, int n_assign, int k,
