@@ -9,6 +9,10 @@ from .moe_oracle import (  # noqa: F401
     select_topk,
     route,
     selection_weights,
+    e4m3_values,
+    e4m3_encode,
+    quantize_fp8,
+    dequantize_fp8,
     capacity_slots,
     capacity_feasible,
     select_capacity,

@@ -12,6 +12,8 @@ Sources (pages are cited by title/address and section):
      weight under the 0.05 threshold and renormalise), the expert layer (every
      expert is an independent two-layer FFN) and the fusion layer (the output
      is the gate-weighted sum of the chosen experts' outputs).
+     Section 4.1 (model loading and memory budget): the resident experts'
+     weights are quantised to 8 bits.
      Section 3.2, second routing pitfall: a per-expert selection capacity of
      tokens*k/experts*1.2; over-capacity experts get -inf and the token
      chooses again (the capacity-limited routing variant).
@@ -48,6 +50,9 @@ the design notes of the repository):
 * row order inside an expert: ascending token id (a stable counting sort);
 * expert FFN: ``silu(x @ W1[e]) @ W2[e]``, silu(u) = u / (1 + exp(-u)), no
   biases; shared expert: the same form with weight 1;
+* low-precision experts: fp8 e4m3 codes with one fp32 scale per expert and
+  output column (max|W|/448), round-to-nearest-even in float32; the layer is
+  evaluated with the dequantised weights;
 * capacity-limited routing: capacity = ceil(T*k/E*factor); tokens choose in
   ascending id among experts not yet full (serial priority by token id);
   capacity counts selections, before any drop.
@@ -162,6 +167,65 @@ def selection_weights(logits: np.ndarray, ids: np.ndarray, drop_thresh: float = 
         w = np.where(keep, w, 0.0)
         w = w / w.sum(axis=1, keepdims=True)
     return w, keep
+
+
+# ------------------------------------------------- low-precision expert weights --
+# [P1] section 4.1 (model loading and memory budget): the resident experts'
+# FFN weights are quantised to 8 bits (INT8 there) because their
+# distribution is concentrated, halving their memory. Reading taken here for
+# MI355X: 8-bit OCP fp8 e4m3 codes with one fp32 scale per expert and output
+# column, s = max_k |W[e,k,n]| / 448 (448 = largest finite e4m3 value; an
+# all-zero column gets s = 1), codes = e4m3 round-to-nearest-even of W / s,
+# both steps in float32. The quantised layer is the layer evaluated with the
+# dequantised weights s * value(code).
+
+def e4m3_values() -> np.ndarray:
+    """Value of every OCP fp8 e4m3 code (sign, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 is subnormal; 0x7F/0xFF are NaN; no inf)."""
+    v = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sgn, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            v[c] = np.nan
+            continue
+        mag = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        v[c] = -mag if sgn else mag
+    return v
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest finite e4m3 value to each x, ties to the even code, saturating at
+    448; the sign bit is the sign of x (so -0.0 -> 0x80). x must be finite.
+    The two candidates are the neighbouring codes of |x| in the increasing
+    table of the 127 non-negative finite values."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("e4m3_encode: non-finite input")
+    mags = e4m3_values()[:0x7F]                        # codes 0x00..0x7E, increasing
+    a = np.minimum(np.abs(x), mags[-1])                # beyond 448 the nearest finite value is 448
+    hi = np.minimum(np.searchsorted(mags, a, side="left"), 0x7E)   # first code with value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (pick | sign).astype(np.uint8)
+
+
+def quantize_fp8(W: np.ndarray):
+    """Per expert and output column: s = max|W| / 448 and codes = e4m3(W / s), in
+    float32. W: [E,K,N] (any float dtype, converted exactly to float32).
+    Returns (codes uint8 [E,K,N], scales float32 [E,N])."""
+    W32 = np.asarray(W, dtype=np.float32)
+    amax = np.abs(W32).max(axis=1)                       # [E,N], exact
+    s = (amax / np.float32(448.0)).astype(np.float32)    # one IEEE float32 division
+    s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    ratio = (W32 / s[:, None, :]).astype(np.float32)     # float32 division, rounded once
+    return e4m3_encode(ratio), s
+
+
+def dequantize_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """W_deq[e,k,n] = scales[e,n] * value(codes[e,k,n]) in float64."""
+    return e4m3_values()[codes.astype(np.int64)] * scales.astype(np.float64)[:, None, :]
 
 
 # ------------------------------------------------- capacity-limited routing --
