@@ -261,6 +261,54 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
                 int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* inv,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Low-precision experts: fp8 (OCP e4m3) expert weights.
+ *
+ * Page 1 ("MoE大模型的智能调度…", www.jsqmd.com/news/1091713), section 4.1
+ * (model loading and memory budget): the experts kept resident store their
+ * FFN weights in 8 bits, halving their memory. The 8-bit format here is OCP
+ * fp8 e4m3 with one fp32 scale per expert and output column:
+ *
+ *   scale[e][n]   = max_k |W[e][k][n]| / 448        (1.0 for an all-zero column)
+ *   code[e][k][n] = e4m3(W[e][k][n] / scale[e][n])  nearest, ties to even,
+ *                                                   saturating at +-448
+ *
+ * both divisions IEEE fp32. The dequantised weight is scale * value(code):
+ * the matrix cores take the codes widened exactly to bf16, and the scale
+ * multiplies each column's fp32 sums.
+ *
+ * Tiled code layout of Wq (device memory, caller-owned, moe_fp8_weight_bytes
+ * bytes): for each expert e, 8 KiB tiles of 128 columns x 64 k; tile
+ * (nb, kb) starts at byte ((e*NB + nb)*(K/64) + kb)*8192, NB = ceil(N/128).
+ * Inside a tile, the code of (n, k) (tile-relative) is at byte
+ *     n*64 + ((k/8) ^ (((n >> 1) & 7) ^ ((n >> 4) & 1)))*8 + k%8.
+ * Columns at or past N hold code 0.
+ *
+ * moe_fp8_weight_bytes: bytes of Wq for E matrices [K][N]; 0 when a size is
+ *   < 1 or K % 64 != 0.
+ * moe_quantize_fp8: W [E][K][N] dt, finite values -> Wq and scales [E][N]
+ *   fp32. K % 64 == 0, else MOE_ERR_UNSUPPORTED. W1 [E,H,F] is quantised
+ *   with (K, N) = (H, F), W2 [E,F,H] with (F, H).
+ * moe_grouped_ffn_fp8: moe_grouped_ffn on the dequantised weights with bf16
+ *   activations (x_perm bf16, h bf16, y_perm fp32) and no shared expert.
+ *   H and F multiples of 64 and >= 128, else MOE_ERR_UNSUPPORTED.
+ *   ws: moe_ffn_workspace_bytes(T,F,E,k,0,MOE_BF16) bytes.
+ * moe_forward_fp8: moe_forward with these experts; x and Wr bf16 (the router
+ *   keeps bf16 operands and fp32 logits), no shared expert. Outputs, debug
+ *   outputs and workspace as moe_forward with Fs = 0, dt = MOE_BF16.
+ */
+size_t moe_fp8_weight_bytes(int E, int K, int N);
+int moe_quantize_fp8(const void* W, int E, int K, int N, moe_dtype_t dt, uint8_t* Wq, float* scales,
+                     hipStream_t stream);
+int moe_grouped_ffn_fp8(const void* x_perm, const int32_t* expert_offsets, const uint8_t* W1q,
+                        const float* W1_scale, const uint8_t* W2q, const float* W2_scale, int T, int H,
+                        int F, int E, int k, float* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+int moe_forward_fp8(const void* x, const void* Wr, const float* bias, const uint8_t* W1q,
+                    const float* W1_scale, const uint8_t* W2q, const float* W2_scale, int T, int H, int F,
+                    int E, int k, float drop_thresh, void* y, moe_dtype_t out_dt, int32_t* topk_ids,
+                    float* topk_w, int32_t* expert_offsets, int32_t* inv, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

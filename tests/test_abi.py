@@ -16,7 +16,7 @@ moe = pytest.importorskip("top_routing_grouped_gemm_amd")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -168,6 +168,46 @@ def test_permute_ffn_combine_forward_reject(lib):
     bad = list(args)
     bad[16] = 5
     assert lib.moe_forward(*bad) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_rejects(lib):
+    N = None
+    bf16 = 1
+    # tiled code bytes: E * ceil(N/128)*128 * K; K must be a multiple of 64
+    assert lib.moe_fp8_weight_bytes(128, 2048, 768) == 128 * 768 * 2048
+    assert lib.moe_fp8_weight_bytes(2, 64, 100) == 2 * 128 * 64
+    assert lib.moe_fp8_weight_bytes(2, 96, 128) == 0
+    assert lib.moe_fp8_weight_bytes(0, 64, 128) == 0
+    assert lib.moe_quantize_fp8(_p(), 2, 96, 128, bf16, _p(), _p(), N) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_fp8(_p(), 2, 64, 128, 5, _p(), _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(_p(), 0, 64, 128, bf16, _p(), _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(_p(), 2, 64, 128, bf16, N, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    # grouped ffn: H, F multiples of 64 and >= 128
+    need = lib.moe_ffn_workspace_bytes(64, 256, 4, 2, 0, bf16)
+
+    def ffn(H=256, F=256, ws=need, y=_p()):
+        return lib.moe_grouped_ffn_fp8(_p(), _p(), _p(), _p(), _p(), _p(), 64, H, F, 4, 2, y, _p(), ws, N)
+
+    assert ffn(H=96) == moe.MOE_ERR_UNSUPPORTED
+    assert ffn(F=64) == moe.MOE_ERR_UNSUPPORTED
+    assert ffn(ws=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert ffn(y=N) == moe.MOE_ERR_INVALID_ARG
+    # forward
+    need = lib.moe_workspace_bytes(64, 256, 256, 4, 2, 0, bf16)
+    args = [_p(), _p(), N, _p(), _p(), _p(), _p(), 64, 256, 256, 4, 2, 0.0, _p(), 0, N, N, N, N, _p(), need, N]
+    assert len(args) == len(lib.moe_forward_fp8.argtypes)
+    bad = list(args)
+    bad[20] = need - 1
+    assert lib.moe_forward_fp8(*bad) == moe.MOE_ERR_WORKSPACE
+    bad = list(args)
+    bad[4] = N  # W1 scales
+    assert lib.moe_forward_fp8(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[8] = 200  # H % 64 != 0
+    assert lib.moe_forward_fp8(*bad) == moe.MOE_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[12] = 0.7
+    assert lib.moe_forward_fp8(*bad) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_binding_raises_without_library(tmp_path):

@@ -19,11 +19,15 @@ from ._binding import (  # noqa: F401
     moe_combine,
     moe_ffn_workspace_bytes,
     moe_forward,
+    moe_forward_fp8,
+    moe_fp8_weight_bytes,
     moe_grouped_ffn,
+    moe_grouped_ffn_fp8,
     moe_grouped_ffn_padded,
     moe_pad_dispatch,
     moe_permute,
     moe_permute_workspace_bytes,
+    moe_quantize_fp8,
     moe_route,
     moe_route_capacity,
     moe_route_workspace_bytes,

@@ -22,7 +22,8 @@ EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_work
            "moe_permute_workspace_bytes", "moe_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_forward", "moe_route_capacity_workspace_bytes", "moe_route_capacity",
            "moe_select_capacity_workspace_bytes", "moe_select_capacity", "moe_pad_dispatch",
-           "moe_grouped_ffn_padded_workspace_bytes", "moe_grouped_ffn_padded")
+           "moe_grouped_ffn_padded_workspace_bytes", "moe_grouped_ffn_padded", "moe_fp8_weight_bytes",
+           "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_forward_fp8")
 
 
 class MoEError(RuntimeError):
@@ -82,6 +83,15 @@ def load_library(path: Optional[str] = None):
     lib.moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp, vp,
                                 vp, vp, vp, sz, vp]
     lib.moe_forward.restype = i32
+    lib.moe_fp8_weight_bytes.argtypes = [i32, i32, i32]
+    lib.moe_fp8_weight_bytes.restype = sz
+    lib.moe_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_quantize_fp8.restype = i32
+    lib.moe_grouped_ffn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+    lib.moe_grouped_ffn_fp8.restype = i32
+    lib.moe_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, vp, vp,
+                                    vp, sz, vp]
+    lib.moe_forward_fp8.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -286,4 +296,58 @@ def moe_forward(x, Wr, bias, W1, W2, k: int, drop_thresh: float = 0.0, W1s=None,
                                     _ptr(topk_w), _ptr(expert_offsets), _ptr(inv), _ptr(ws), ws.numel(),
                                     _stream(stream))
     _check(st, "moe_forward")
+    return y
+
+
+def moe_fp8_weight_bytes(E: int, K: int, N: int) -> int:
+    return int(load_library().moe_fp8_weight_bytes(E, K, N))
+
+
+def moe_quantize_fp8(W, Wq=None, scales=None, stream=None):
+    """fp8 e4m3 codes of W [E,K,N] (bf16 or fp32) in the tiled layout of
+    include/moe.h, with per-expert, per-column fp32 scales.
+    Returns (Wq uint8 [moe_fp8_weight_bytes(E,K,N)], scales [E,N] fp32)."""
+    E, K, N = W.shape
+    dev = W.device
+    nbytes = moe_fp8_weight_bytes(E, K, N)
+    if nbytes == 0:
+        _check(MOE_ERR_UNSUPPORTED, "moe_fp8_weight_bytes")
+    Wq = torch.empty(nbytes, dtype=torch.uint8, device=dev) if Wq is None else Wq
+    scales = torch.empty((E, N), dtype=torch.float32, device=dev) if scales is None else scales
+    st = load_library().moe_quantize_fp8(_ptr(W), E, K, N, _dt(W), _ptr(Wq), _ptr(scales), _stream(stream))
+    _check(st, "moe_quantize_fp8")
+    return Wq, scales
+
+
+def moe_grouped_ffn_fp8(x_perm, expert_offsets, W1q, W1_scale, W2q, W2_scale, T: int, k: int, y_perm=None, ws=None,
+                        stream=None):
+    """Grouped FFN on fp8 experts (scales W1_scale [E,F], W2_scale [E,H]). Returns y_perm [T*k,H] fp32."""
+    E, F = W1_scale.shape
+    H = W2_scale.shape[1]
+    dev = x_perm.device
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
+    need = moe_ffn_workspace_bytes(T, F, E, k, 0, torch.bfloat16)
+    ws = _ws(need, dev) if ws is None else ws
+    st = load_library().moe_grouped_ffn_fp8(_ptr(x_perm), _ptr(expert_offsets), _ptr(W1q), _ptr(W1_scale), _ptr(W2q),
+                                            _ptr(W2_scale), T, H, F, E, k, _ptr(y_perm), _ptr(ws), ws.numel(),
+                                            _stream(stream))
+    _check(st, "moe_grouped_ffn_fp8")
+    return y_perm
+
+
+def moe_forward_fp8(x, Wr, bias, W1q, W1_scale, W2q, W2_scale, k: int, drop_thresh: float = 0.0,
+                    out_dtype=torch.float32, y=None, topk_ids=None, topk_w=None, expert_offsets=None, inv=None,
+                    ws=None, stream=None):
+    """The whole layer with fp8 experts (x, Wr bf16). Returns y [T,H]."""
+    T, H = x.shape
+    E, F = W1_scale.shape
+    dev = x.device
+    y = torch.empty((T, H), dtype=out_dtype, device=dev) if y is None else y
+    need = moe_workspace_bytes(T, H, F, E, k, 0, torch.bfloat16)
+    ws = _ws(need, dev) if ws is None else ws
+    st = load_library().moe_forward_fp8(_ptr(x), _ptr(Wr), _ptr(bias), _ptr(W1q), _ptr(W1_scale), _ptr(W2q),
+                                        _ptr(W2_scale), T, H, F, E, k, float(drop_thresh), _ptr(y), _dt(y),
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(inv), _ptr(ws),
+                                        ws.numel(), _stream(stream))
+    _check(st, "moe_forward_fp8")
     return y

@@ -287,10 +287,19 @@ __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, lon
         }
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN>
+// fp8 B operand (F8B): expert weights as OCP e4m3 codes in 8 KiB tiles of
+// 128 output columns x 64 k, laid out [N/128][K/64][128 n][64 k] per expert,
+// with the 8-byte k-chunk c of column n stored at chunk c ^ f8_swz(n). A
+// stage then copies whole tiles verbatim; a B fragment (8 k-consecutive codes
+// of one column) is one ds_read_b64, and the swizzle spreads the 32 columns a
+// read touches over distinct bank groups both for 16- and for 32-lane phases.
+constexpr int kF8TileN = 128, kF8TileK = 64, kF8TileBytes = kF8TileN * kF8TileK;
+__host__ __device__ __forceinline__ int f8_swz(int n) { return ((n >> 1) & 7) ^ ((n >> 4) & 1); }
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, bool F8B = false>
 struct Tile32 {
     static constexpr int NW = WM * WN;
-    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * (F8B ? 1 : 2), STAGE = A_BYTES + B_BYTES;
     static constexpr int A_CHUNKS = A_BYTES / (1024 * NW), B_CHUNKS = B_BYTES / (1024 * NW);
     static constexpr int LOADS = A_CHUNKS + B_CHUNKS;          // vm ops per lane per stage
     static constexpr int A_RCH = BK / 8, A_RPK = 1024 / (BK * 2);
@@ -300,6 +309,7 @@ struct Tile32 {
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole KiB chunks per wave");
     static_assert(BN * 2 <= 1024 && BK * 2 <= 1024 && (BK == 32 || BK == 64), "row sizes");
     static_assert(BN >= 128, "swz_b32 XORs chunk indices with up to 12: rows need >= 16 chunks of 8 columns");
+    static_assert(!F8B || (BK == kF8TileK && BN % kF8TileN == 0), "fp8 B stages are whole 128 x 64 tiles");
     static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
@@ -309,15 +319,21 @@ struct Tile32 {
 // lda = K, a_kstep = 1; the k-blocked layout written by store_tile32 with
 // c_cap = cap is lda = 32, a_kstep = cap (BK == 32 only).
 // c_cap: 0 for a row-major C with leading dimension ldc, else the k-blocked C.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
+// F8B: B holds the fp8 tiles described at f8_swz (strideB in bytes per
+// expert, ldb unused) and bscale[e*N + n] the fp32 scale of column n of
+// expert e, applied to the fp32 accumulators before the epilogue. The codes
+// widen exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1), so the MFMAs
+// are the bf16 ones and sum_k a*code is exact up to fp32 accumulation.
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool F8B = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t* __restrict__ A, long lda,
                                                                  long a_kstep, const int32_t* __restrict__ a_rows,
-                                                                 const uint16_t* __restrict__ B, long strideB,
-                                                                 long ldb, void* __restrict__ C, long ldc, long c_cap,
+                                                                 const void* __restrict__ B, long strideB, long ldb,
+                                                                 const float* __restrict__ bscale,
+                                                                 void* __restrict__ C, long ldc, long c_cap,
                                                                  const int32_t* __restrict__ offsets, int E,
                                                                  int fixed_rows, int rmin, int rmax, int N, int K,
                                                                  int n_tiles) {
-    using Tl = Tile32<BM, BN, BK, NS, WM, WN>;
+    using Tl = Tile32<BM, BN, BK, NS, WM, WN, F8B>;
     constexpr int NW = Tl::NW, TM = Tl::TM, TN = Tl::TN, WTM = Tl::WTM, WTN = Tl::WTN;
     constexpr int A_BYTES = Tl::A_BYTES, STAGE = Tl::STAGE, LOADS = Tl::LOADS;
     __shared__ __align__(1024) uint8_t smem[NS * STAGE];
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     int e, rb, re, nt;
     if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, rmin, rmax, e, rb, re, nt)) return;
     const int n0 = nt * BN;
-    const uint16_t* Be = B + (long)e * strideB;
+    const uint8_t* Be = (const uint8_t*)B + (long)e * strideB * (F8B ? 1 : 2);
     const int wave = threadIdx.x / kWave, l = lane_id();
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
 
@@ -339,13 +355,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
         if (a_rows != nullptr) grow = a_rows[grow];
         a_src[i] = A + (long)grow * lda + swz_a32<BK>(row, l % Tl::A_RCH) * 8;
     }
-    const uint16_t* b_src[Tl::B_CHUNKS];
+    const uint8_t* b_src[Tl::B_CHUNKS];
+    long b_kbytes;  // bytes of B per unit of k0
+    if constexpr (F8B) {
+        const int nb_last = (N + kF8TileN - 1) / kF8TileN - 1;
 #pragma unroll
-    for (int i = 0; i < Tl::B_CHUNKS; ++i) {
-        const int c = uwave + NW * i;
-        const int row = c * Tl::B_RPK + l / Tl::B_RCH;
-        const int col = min(n0 + swz_b32(row, l % Tl::B_RCH) * 8, N - 8);  // columns past N repeat a valid chunk
-        b_src[i] = Be + (long)row * ldb + col;
+        for (int i = 0; i < Tl::B_CHUNKS; ++i) {
+            const int c = uwave + NW * i;  // KiB chunk of the stage's B tiles
+            const int nb = min(n0 / kF8TileN + c / (kF8TileBytes / 1024), nb_last);  // tiles past N repeat the last
+            b_src[i] = Be + (long)nb * (K / kF8TileK) * kF8TileBytes + (c % (kF8TileBytes / 1024)) * 1024 + 16 * l;
+        }
+        b_kbytes = kF8TileBytes / kF8TileK;
+    } else {
+#pragma unroll
+        for (int i = 0; i < Tl::B_CHUNKS; ++i) {
+            const int c = uwave + NW * i;
+            const int row = c * Tl::B_RPK + l / Tl::B_RCH;
+            const int col = min(n0 + swz_b32(row, l % Tl::B_RCH) * 8, N - 8);  // columns past N repeat a valid chunk
+            b_src[i] = Be + ((long)row * ldb + col) * 2;
+        }
+        b_kbytes = ldb * 2;
     }
     lds_u8* ring = (lds_u8*)smem;
     auto issue = [&](int stage, int k0) {
@@ -353,7 +382,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
 #pragma unroll
         for (int i = 0; i < Tl::A_CHUNKS; ++i) lds_dma16(a_src[i] + (long)k0 * a_kstep, b0 + i * 1024 * NW);
 #pragma unroll
-        for (int i = 0; i < Tl::B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * ldb, b0 + A_BYTES + i * 1024 * NW);
+        for (int i = 0; i < Tl::B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * b_kbytes, b0 + A_BYTES + i * 1024 * NW);
     };
 
     f32x16 acc[TM][TN];
@@ -376,6 +405,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
         for (int i = 0; i < TM; ++i) {
             const int row = wm * WTM + i * 32 + (l & 31);
             af[i] = *(lds_bf16x8*)(As + row * (BK * 2) + swz_a32<BK>(row, (ks >> 3) + (l >> 5)) * 16);
+        }
+        if constexpr (F8B) {
+            typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+            const int kc = (ks >> 3) + (l >> 5);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = wn * WTN + j * 32 + (l & 31);
+                const int nn = n % kF8TileN;
+                const u32x2 q = *(lds_u32x2*)(Bs + (n / kF8TileN) * kF8TileBytes + nn * kF8TileK +
+                                              ((kc ^ f8_swz(nn)) << 3));
+                const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
+                const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true);
+                const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false);
+                const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true);
+                typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+                const bf16x4 lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
+                const bf16x4 hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3);
+                bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            return;
         }
         const int G = l >> 4, j4 = l & 15;
 #pragma unroll
@@ -434,6 +484,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     }
     if (!active) return;
     mma(fa[1], fb[1]);
+    if constexpr (F8B) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = min(n0 + wn * WTN + j * 32 + (l & 31), N - 1);
+            const float sc = bscale[(long)e * N + col];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] *= sc;
+        }
+    }
 
     store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, wm, wn);
 }

@@ -264,9 +264,49 @@ hipError_t run_dma(const void* A, long lda, long a_kstep, const int32_t* a_rows,
     const long grid = max_mtiles(C::BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
-                       dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_kstep, a_rows, (const uint16_t*)B,
-                       strideB, ldb, Cm, ldc, c_cap, offsets, E, fixed_rows, rmin, rmax, N, K, n_tiles);
+                       dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_kstep, a_rows, B, strideB, ldb,
+                       nullptr, Cm, ldc, c_cap, offsets, E, fixed_rows, rmin, rmax, N, K, n_tiles);
     return hipGetLastError();
+}
+
+// fp8-weight shapes (gemm32_kernel with F8B): a B stage is whole 128 x 64
+// code tiles, so BK is 64 and the byte count per stage halves. The streaming
+// shape keeps ~80 KB of weight loads in flight per CU with 6 stages (two
+// workgroups of 72 KB); the large shape's 64-wide k-stages also give A
+// 128-byte row pieces.
+using F8Stream = DmaCfg<32, 128, 64, 6, 1, 4>;
+using F8Large = DmaCfg<256, 256, 64, 3, 4, 2>;
+
+template <class C, int EPI>
+hipError_t run_dma8(const void* A, long lda, const int32_t* a_rows, const void* Bq, long strideB, const float* bscale,
+                    void* Cm, long ldc, long c_cap, const int32_t* offsets, int E, int max_rows, int N, int K,
+                    hipStream_t s, int rmin = 0, int rmax = INT_MAX) {
+    const int n_tiles = (N + C::BN - 1) / C::BN;
+    const long grid = max_mtiles(C::BM, offsets, E, 0, max_rows) * n_tiles + dma::kXcds;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI, true>),
+                       dim3((unsigned)grid), dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, 1L, a_rows, Bq,
+                       strideB, 0L, bscale, Cm, ldc, c_cap, offsets, E, 0, rmin, rmax, N, K, n_tiles);
+    return hipGetLastError();
+}
+
+// The three row regimes of choose_tile on the fp8 shapes.
+template <int EPI>
+hipError_t run_fp8_cfg(TileCfg cfg, const void* A, long lda, const int32_t* a_rows, const void* Bq, long strideB,
+                       const float* bscale, void* Cm, long ldc, long c_cap, const int32_t* offsets, int E,
+                       int max_rows, int N, int K, hipStream_t s) {
+    if (cfg == kTileM128)
+        return run_dma8<F8Large, EPI>(A, lda, a_rows, Bq, strideB, bscale, Cm, ldc, c_cap, offsets, E, max_rows, N, K,
+                                      s);
+    if (cfg == kTileMixed) {
+        const hipError_t e = run_dma8<F8Stream, EPI>(A, lda, a_rows, Bq, strideB, bscale, Cm, ldc, c_cap, offsets, E,
+                                                     max_rows, N, K, s, 0, kStreamRows);
+        if (e != hipSuccess) return e;
+        return run_dma8<F8Large, EPI>(A, lda, a_rows, Bq, strideB, bscale, Cm, ldc, c_cap, offsets, E, max_rows, N, K,
+                                      s, kStreamRows, INT_MAX);
+    }
+    return run_dma8<F8Stream, EPI>(A, lda, a_rows, Bq, strideB, bscale, Cm, ldc, c_cap, offsets, E, max_rows, N, K,
+                                   s);
 }
 
 template <class C>
@@ -388,6 +428,24 @@ hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, 
     }
     return run_dma<DmaStream, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows, H,
                                             F, s);
+}
+
+bool ffn_fp8_ok(int H, int F) { return H % 64 == 0 && F % 64 == 0 && H >= 128 && F >= 128; }
+
+hipError_t launch_ffn_up_fp8(const void* A, const int32_t* a_rows, const int32_t* offsets, int E, int max_rows,
+                             const uint8_t* W1q, const float* s1, int H, int F, TileCfg cfg, void* h, hipStream_t s) {
+    const long strideB = fp8_weight_bytes(1, H, F);
+    return run_fp8_cfg<kEpiSiluOut>(cfg, A, H, a_rows, W1q, strideB, s1, h, F, 0, offsets, E, max_rows, F, H, s);
+}
+
+hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int max_rows, const uint8_t* W2q,
+                               const float* s2, int F, int H, TileCfg cfg, bool packed, void* y, long cap,
+                               hipStream_t s) {
+    const long strideB = fp8_weight_bytes(1, F, H);
+    if (packed)
+        return run_fp8_cfg<kEpiPacked24>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, cap, offsets, E, max_rows, H, F,
+                                         s);
+    return run_fp8_cfg<kEpiF32Out>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, 0, offsets, E, max_rows, H, F, s);
 }
 
 TileCfg choose_tile(long rows, int groups) {

@@ -386,4 +386,73 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
     return hip_status(moe::launch_combine(y_perm, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
 }
 
+size_t moe_fp8_weight_bytes(int E, int K, int N) {
+    if (E < 1 || K < 1 || N < 1 || E > kMaxExperts || K % 64 != 0) return 0;
+    return (size_t)moe::fp8_weight_bytes(E, K, N);
+}
+
+int moe_quantize_fp8(const void* W, int E, int K, int N, moe_dtype_t dt, uint8_t* Wq, float* scales,
+                     hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    if (E < 1 || K < 1 || N < 1) return MOE_ERR_INVALID_ARG;
+    if (E > kMaxExperts || K % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((long long)E * ((N + 127) / 128) * (K / 64) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;  // tile grid
+    if (!W || !Wq || !scales) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_quantize_fp8(W, E, K, N, (Dtype)dt, Wq, scales, stream));
+}
+
+int moe_grouped_ffn_fp8(const void* x_perm, const int32_t* expert_offsets, const uint8_t* W1q, const float* W1_scale,
+                        const uint8_t* W2q, const float* W2_scale, int T, int H, int F, int E, int k, float* y_perm,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if (!moe::ffn_fp8_ok(H, F)) return MOE_ERR_UNSUPPORTED;
+    if (!x_perm || !expert_offsets || !W1q || !W1_scale || !W2q || !W2_scale || !y_perm || !ws)
+        return MOE_ERR_INVALID_ARG;
+    const FfnLayout L = ffn_layout(T, F, k, 0, MOE_BF16);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const int rows = T * k;
+    const moe::TileCfg cfg = moe::choose_tile(rows, E);
+    void* h = (char*)ws + L.h;
+    MOE_TRY(moe::launch_ffn_up_fp8(x_perm, nullptr, expert_offsets, E, rows, W1q, W1_scale, H, F, cfg, h, stream));
+    return hip_status(
+        moe::launch_ffn_down_fp8(h, expert_offsets, E, rows, W2q, W2_scale, F, H, cfg, false, y_perm, 0, stream));
+}
+
+int moe_forward_fp8(const void* x, const void* Wr, const float* bias, const uint8_t* W1q, const float* W1_scale,
+                    const uint8_t* W2q, const float* W2_scale, int T, int H, int F, int E, int k, float drop_thresh,
+                    void* y, moe_dtype_t out_dt, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                    int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if (!moe::ffn_fp8_ok(H, F)) return MOE_ERR_UNSUPPORTED;
+    if (!x || !Wr || !W1q || !W1_scale || !W2q || !W2_scale || !y || !ws) return MOE_ERR_INVALID_ARG;
+    const FwdLayout L = fwd_layout(T, H, F, E, k, 0, MOE_BF16);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + L.ids);
+    float* w = topk_w ? topk_w : (float*)(base + L.w);
+    int32_t* off = expert_offsets ? expert_offsets : (int32_t*)(base + L.offsets);
+    int32_t* iv = inv ? inv : (int32_t*)(base + L.inv);
+    int32_t* row_token = (int32_t*)(base + L.row_token);
+    int32_t* partial = (int32_t*)(base + L.partial);
+    void* y_planes = base + L.y_perm;
+    void* h = base + L.ffn + ffn_layout(T, F, k, 0, MOE_BF16).h;
+    const int rows = T * k;
+    const moe::TileCfg cfg = moe::choose_tile(rows, E);
+    // the W1 launch gathers x rows through row_token (no permuted copy); the W2 launch writes 24-bit y_perm planes
+    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, moe::kBF16, ids, w, base + L.route, stream));
+    if ((st = enqueue_permute(x, ids, w, T, H, E, k, MOE_BF16, nullptr, off, row_token, iv, partial, false,
+                              stream)) != MOE_OK)
+        return st;
+    MOE_TRY(moe::launch_ffn_up_fp8(x, row_token, off, E, rows, W1q, W1_scale, H, F, cfg, h, stream));
+    MOE_TRY(moe::launch_ffn_down_fp8(h, off, E, rows, W2q, W2_scale, F, H, cfg, true, y_planes, rows, stream));
+    return hip_status(moe::launch_combine_packed(y_planes, rows, iv, w, nullptr, T, H, k, (moe::Dtype)out_dt, y,
+                                                 stream));
+}
+
 }  // extern "C"

@@ -79,6 +79,22 @@ bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt);
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
                                 const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s);
 
+// fp8 expert weights (fp8_quant.hip): bytes of the tiled codes of E matrices
+// [K][N], and the quantiser (scales[E][N] fp32, codes in the tiled layout).
+long fp8_weight_bytes(int E, int K, int N);
+hipError_t launch_quantize_fp8(const void* W, int E, int K, int N, Dtype dt, uint8_t* Wq, float* scales,
+                               hipStream_t s);
+// Grouped FFN on fp8 weights (bf16 activations): W1 [E][H][F] and W2 [E][F][H]
+// as tiled codes with per-column scales. a_rows != NULL gathers the W1 A rows
+// from x through the row -> token map; packed: y as the 24-bit planes of
+// ffn_down_packs, else fp32 y[rows][H].
+bool ffn_fp8_ok(int H, int F);
+hipError_t launch_ffn_up_fp8(const void* A, const int32_t* a_rows, const int32_t* offsets, int E, int max_rows,
+                             const uint8_t* W1q, const float* s1, int H, int F, TileCfg cfg, void* h, hipStream_t s);
+hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int max_rows, const uint8_t* W2q,
+                               const float* s2, int F, int H, TileCfg cfg, bool packed, void* y, long cap,
+                               hipStream_t s);
+
 // y_perm given as the two planes of ffn_down_packs (cap = row capacity).
 hipError_t launch_combine_packed(const void* y_planes, long cap, const int32_t* inv, const float* w,
                                  const float* y_shared, int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
