@@ -261,6 +261,55 @@ def padded_times(name, reps=10):
             "grouped_ffn_speedup_of_ragged": round(pad["grouped_ffn"] / rag["grouped_ffn"], 3)}
 
 
+def fp8_times(name, steps=20, reps=20):
+    """fp8 expert weights next to bf16 on one workload: the one-time quantisation, the whole layer
+    (moe_forward_fp8 against moe_forward) and the grouped FFN alone (HIP events), with the weight bytes each
+    streams (fp8: one byte per weight plus the per-column scales)."""
+    import torch
+
+    import gen
+    import top_routing_grouped_gemm_amd as moe
+
+    dev = torch.device("cuda:0")
+    I = gen.make_inputs(name)
+    d = gen.to_device(I, dev)
+    s = torch.cuda.current_stream()
+    T, H, F, E, k = I.T, I.H, I.F, I.E, I.k
+    W1q, s1 = moe.moe_quantize_fp8(d["W1"])
+    W2q, s2 = moe.moe_quantize_fp8(d["W2"])
+    t_quant = event_time_ms(lambda: (moe.moe_quantize_fp8(d["W1"], Wq=W1q, scales=s1),
+                                     moe.moe_quantize_fp8(d["W2"], Wq=W2q, scales=s2)), 3, s)
+    ws = torch.empty(moe.moe_workspace_bytes(T, H, F, E, k, 0, torch.bfloat16), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    fwd8 = event_time_ms(lambda: moe.moe_forward_fp8(d["x"], d["Wr"], d["bias"], W1q, s1, W2q, s2, k, I.drop, y=y,
+                                                     ws=ws), steps, s)
+    fwd16 = event_time_ms(lambda: moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], k, I.drop, y=y,
+                                                  ws=ws), steps, s)
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop)
+    x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, E)
+    torch.cuda.synchronize()
+    counts = (off[1:] - off[:-1]).cpu()
+    hit, A = int((counts > 0).sum()), int(counts.sum())
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    fws = torch.empty(moe.moe_ffn_workspace_bytes(T, F, E, k, 0, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ffn8 = event_time_ms(lambda: moe.moe_grouped_ffn_fp8(x_perm, off, W1q, s1, W2q, s2, T, k, y_perm=y_perm, ws=fws),
+                         reps, s)
+    ffn16 = event_time_ms(lambda: moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm, ws=fws),
+                          reps, s)
+    w8 = hit * (2 * H * F + 4 * (H + F))
+    w16 = hit * 2 * H * F * 2
+    flops = 4.0 * A * H * F
+    return {"workload": name, "T": T, "H": H, "F": F, "E": E, "k": k, "A": A, "experts_hit": hit,
+            "quantize_ms_once": round(t_quant, 3),
+            "forward_ms": {"fp8": round(fwd8, 5), "bf16": round(fwd16, 5)},
+            "tokens_per_s": {"fp8": round(T / (fwd8 * 1e-3), 1), "bf16": round(T / (fwd16 * 1e-3), 1)},
+            "grouped_ffn_ms": {"fp8": round(ffn8, 5), "bf16": round(ffn16, 5)},
+            "weight_bytes": {"fp8": w8, "bf16": w16},
+            "weight_stream_gbs": {"fp8": round(w8 / (ffn8 * 1e-3) / 1e9, 1), "bf16": round(w16 / (ffn16 * 1e-3) / 1e9, 1)},
+            "grouped_ffn_tflops": {"fp8": round(flops / (ffn8 * 1e-3) / 1e12, 1),
+                                   "bf16": round(flops / (ffn16 * 1e-3) / 1e12, 1)}}
+
+
 def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
     """The fp64 oracle, as it stands, on the host cores: whole prefill batches, repeated until about 10 s."""
     import numpy as np
@@ -305,6 +354,8 @@ def main():
                     help="with --only: time capacity-limited routing (this factor) against plain routing")
     ap.add_argument("--padded", action="store_true",
                     help="with --only: time the padded fixed-shape layout against the ragged grouped FFN")
+    ap.add_argument("--fp8", action="store_true",
+                    help="with --only: time fp8 expert weights against bf16 (layer and grouped FFN)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -329,6 +380,9 @@ def main():
         return
     if args.only and args.padded:
         print(json.dumps(padded_times(args.only)), flush=True)
+        return
+    if args.only and args.fp8:
+        print(json.dumps(fp8_times(args.only)), flush=True)
         return
     if args.only and args.capacity_factor > 0:
         print(json.dumps(capacity_times(args.only, args.capacity_factor)), flush=True)
@@ -373,6 +427,9 @@ def main():
         dec["weight_stream_hbm_frac"] = round(dec["weight_stream_gbs"] / PEAK_HBM_GBS, 4)
         dec["grouped_ffn_traffic_bytes"] = measured_traffic("traffic_decode_bytes")
         line["decode"] = dec
+        f8 = fp8_times("decode", max(args.steps, 50), max(args.stage_reps, 100))
+        line["decode_fp8_experts"] = {k_: f8[k_] for k_ in ("forward_ms", "tokens_per_s", "grouped_ffn_ms",
+                                                             "weight_bytes", "weight_stream_gbs")}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle) ...")
         line["cpu_baseline"] = cpu_baseline("prefill")

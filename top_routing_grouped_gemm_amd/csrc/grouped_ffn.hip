@@ -271,10 +271,11 @@ hipError_t run_dma(const void* A, long lda, long a_kstep, const int32_t* a_rows,
 
 // fp8-weight shapes (gemm32_kernel with F8B): a B stage is whole 128 x 64
 // code tiles, so BK is 64 and the byte count per stage halves. The streaming
-// shape keeps ~80 KB of weight loads in flight per CU with 6 stages (two
-// workgroups of 72 KB); the large shape's 64-wide k-stages also give A
+// shape runs 3-stage rings of 36 KB, four workgroups per CU (measured at
+// decode: 3 stages x 4 workgroups streamed 4.7-4.8 TB/s of weights, 4 x 3
+// 4.6, 6 x 2 4.1, 8 x 1 3.5); the large shape's 64-wide k-stages also give A
 // 128-byte row pieces.
-using F8Stream = DmaCfg<32, 128, 64, 6, 1, 4>;
+using F8Stream = DmaCfg<32, 128, 64, 3, 1, 4>;
 using F8Large = DmaCfg<256, 256, 64, 3, 4, 2>;
 
 template <class C, int EPI>
