@@ -32,25 +32,8 @@ __device__ __forceinline__ void combine_store(float4 acc, void* __restrict__ y, 
     }
 }
 
-// Four consecutive y_perm values (group idx = row*H/4 + column/4): fp32, or
-// the 24-bit planes written by the W2 epilogue (upper 16 bits, 8 bytes per
-// group; next 8 bits, 4 bytes per group at lo_off bytes), reassembled exactly.
-template <bool PACKED>
-__device__ __forceinline__ float4 load4(const void* __restrict__ yp, long lo_off, long idx) {
-    if constexpr (PACKED) {
-        const u32x2 h = ((const u32x2*)yp)[idx];
-        const uint32_t l = ((const uint32_t*)((const uint8_t*)yp + lo_off))[idx];
-        return make_float4(__uint_as_float((h[0] << 16) | ((l & 0xffu) << 8)),
-                           __uint_as_float((h[0] & 0xffff0000u) | (((l >> 8) & 0xffu) << 8)),
-                           __uint_as_float((h[1] << 16) | (((l >> 16) & 0xffu) << 8)),
-                           __uint_as_float((h[1] & 0xffff0000u) | ((l >> 24) << 8)));
-    } else {
-        return ((const float4*)yp)[idx];
-    }
-}
-
-template <bool OUT_BF16, bool PACKED>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm, long lo_off,
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm,
                                                       const int32_t* __restrict__ inv, const float* __restrict__ w,
                                                       const float4* __restrict__ ysh, int H4, int k,
                                                       void* __restrict__ y) {
@@ -68,8 +51,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                 const int r = j < k ? inv[t * k + j] : -1;
                 ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
                 const long row = (long)(r >= 0 ? r : 0) * H4;
-                v0[u] = r >= 0 ? load4<PACKED>(y_perm, lo_off, row + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
-                v1[u] = (r >= 0 && two) ? load4<PACKED>(y_perm, lo_off, row + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v0[u] = r >= 0 ? y_perm[row + c0] : make_float4(0.f, 0.f, 0.f, 0.f);
+                v1[u] = (r >= 0 && two) ? y_perm[row + c1] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -104,17 +87,90 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     }
 }
 
+// 24-bit planes: each thread owns 8 consecutive columns, read as one 16-byte
+// load of their upper halves and one 8-byte load of their low bytes per slot
+// (wider requests than the 4-column form; the same fmaf sequence per value).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_packed_kernel(const u32x4* __restrict__ hi, const u32x2* __restrict__ lo,
+                                                             const int32_t* __restrict__ inv,
+                                                             const float* __restrict__ w,
+                                                             const float4* __restrict__ ysh, int H8, int k,
+                                                             void* __restrict__ y) {
+    const long t = blockIdx.x;
+    for (int c = threadIdx.x; c < H8; c += 256) {
+        float a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4 vh[8];
+            u32x2 vl[8];
+            float ww[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                const int r = j < k ? inv[t * k + j] : -1;
+                ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
+                const long g = (long)(r >= 0 ? r : 0) * H8 + c;
+                vh[u] = r >= 0 ? hi[g] : u32x4{0u, 0u, 0u, 0u};
+                vl[u] = r >= 0 ? lo[g] : u32x2{0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u < k && ww[u] != 0.0f) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t h16 = (vh[u][i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                        const uint32_t l8 = (vl[u][i >> 2] >> (8 * (i & 3))) & 0xffu;
+                        a[i] = fmaf(ww[u], __uint_as_float((h16 << 16) | (l8 << 8)), a[i]);
+                    }
+                }
+            }
+        }
+        if (ysh != nullptr) {
+            const float4 s0 = ysh[(t * H8 + c) * 2], s1 = ysh[(t * H8 + c) * 2 + 1];
+            a[0] += s0.x;
+            a[1] += s0.y;
+            a[2] += s0.z;
+            a[3] += s0.w;
+            a[4] += s1.x;
+            a[5] += s1.y;
+            a[6] += s1.z;
+            a[7] += s1.w;
+        }
+        if (OUT_BF16) {
+            const u32x4 pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+                              pack_bf16x2(a[6], a[7])};
+            ((u32x4*)y)[t * H8 + c] = pk;
+        } else {
+            ((float4*)y)[(t * H8 + c) * 2] = make_float4(a[0], a[1], a[2], a[3]);
+            ((float4*)y)[(t * H8 + c) * 2 + 1] = make_float4(a[4], a[5], a[6], a[7]);
+        }
+    }
+}
+
 template <bool PACKED>
 hipError_t combine(const void* y_perm, long lo_off, const int32_t* inv, const float* w, const float* y_shared, int T,
                    int H, int k, Dtype out_dt, void* y, hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if constexpr (PACKED) {
+        const u32x4* hi = (const u32x4*)y_perm;
+        const u32x2* lo = (const u32x2*)((const uint8_t*)y_perm + lo_off);
+        if (out_dt == kBF16)
+            hipLaunchKernelGGL((combine_packed_kernel<true>), dim3(T), dim3(256), 0, s, hi, lo, inv, w,
+                               (const float4*)y_shared, H / 8, k, y);
+        else
+            hipLaunchKernelGGL((combine_packed_kernel<false>), dim3(T), dim3(256), 0, s, hi, lo, inv, w,
+                               (const float4*)y_shared, H / 8, k, y);
+        return hipGetLastError();
+    }
     const int H4 = H / 4;
+    const float4* yp = (const float4*)y_perm;
     if (out_dt == kBF16)
-        hipLaunchKernelGGL((combine_kernel<true, PACKED>), dim3(T), dim3(256), 0, s, y_perm, lo_off, inv, w,
-                           (const float4*)y_shared, H4, k, y);
+        hipLaunchKernelGGL((combine_kernel<true>), dim3(T), dim3(256), 0, s, yp, inv, w, (const float4*)y_shared, H4,
+                           k, y);
     else
-        hipLaunchKernelGGL((combine_kernel<false, PACKED>), dim3(T), dim3(256), 0, s, y_perm, lo_off, inv, w,
-                           (const float4*)y_shared, H4, k, y);
+        hipLaunchKernelGGL((combine_kernel<false>), dim3(T), dim3(256), 0, s, yp, inv, w, (const float4*)y_shared, H4,
+                           k, y);
     return hipGetLastError();
 }
 
