@@ -13,6 +13,11 @@ from .moe_oracle import (  # noqa: F401
     e4m3_encode,
     quantize_fp8,
     dequantize_fp8,
+    MX_BLOCK,
+    mx_scale_exponents,
+    quantize_mx,
+    dequantize_mx,
+    expert_ffn_mx,
     capacity_slots,
     capacity_feasible,
     select_capacity,

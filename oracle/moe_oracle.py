@@ -53,6 +53,10 @@ the design notes of the repository):
 * low-precision experts: fp8 e4m3 codes with one fp32 scale per expert and
   output column (max|W|/448), round-to-nearest-even in float32; the layer is
   evaluated with the dequantised weights;
+* MX fp8 (activations and weights in 8 bits on the fp8 matrix cores): OCP MX
+  E4M3 blocks of 32 along each product's reduction axis, shared scale
+  2^(floor(log2 amax) - 8); the token rows are quantised before dispatch, the
+  expert's SiLU output is re-quantised before the second product;
 * capacity-limited routing: capacity = ceil(T*k/E*factor); tokens choose in
   ascending id among experts not yet full (serial priority by token id);
   capacity counts selections, before any drop.
@@ -226,6 +230,62 @@ def quantize_fp8(W: np.ndarray):
 def dequantize_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """W_deq[e,k,n] = scales[e,n] * value(codes[e,k,n]) in float64."""
     return e4m3_values()[codes.astype(np.int64)] * scales.astype(np.float64)[:, None, :]
+
+
+# MX (microscaling) fp8: activations as well as weights in 8 bits, so that the
+# products run on the fp8 matrix cores. Reading: the OCP MX block format with
+# E4M3 elements -- every 32 consecutive values along the reduction axis share
+# one power-of-two scale X = 2^(floor(log2(amax)) - 8) (8 = exponent of the
+# largest E4M3 power of two, 2^8 <= 448 < 2^9), stored as a biased exponent
+# byte (E8M0, bias 127); each value is encoded as e4m3(V / X) with the same
+# rounding and saturation as above (values in [448, 512)·X clamp to 448·X).
+# An all-zero block has X = 1. V / X is exact in float32 (a power-of-two
+# scaling of a float32 value), so the codes depend on the float32 inputs only.
+
+MX_BLOCK = 32
+MX_EMAX_E4M3 = 8
+
+
+def mx_scale_exponents(amax: np.ndarray) -> np.ndarray:
+    """Unbiased shared exponent floor(log2(amax)) - 8 per block (0 for amax == 0),
+    clamped to the E8M0 range [-127, 127]."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)            # amax = m * 2^e, 0.5 <= m < 1: floor(log2(amax)) = e - 1
+    x = np.where(amax > 0, e - 1 - MX_EMAX_E4M3, 0)
+    return np.clip(x, -127, 127).astype(np.int64)
+
+
+def quantize_mx(V: np.ndarray, axis: int):
+    """MX E4M3 of V (any float dtype, converted exactly to float32) with blocks of
+    32 consecutive elements along ``axis`` (its length a multiple of 32).
+    Returns (codes uint8, same shape as V; scale bytes uint8 with that axis
+    divided by 32, value = unbiased exponent + 127)."""
+    V32 = np.asarray(V, dtype=np.float32)
+    Vm = np.moveaxis(V32, axis, -1)
+    n = Vm.shape[-1]
+    if n % MX_BLOCK != 0:
+        raise ValueError("quantize_mx: axis length must be a multiple of 32")
+    blocks = Vm.reshape(Vm.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    xexp = mx_scale_exponents(np.abs(blocks).max(axis=-1))
+    scaled = blocks.astype(np.float64) * np.ldexp(1.0, -xexp)[..., None]   # exact
+    codes = e4m3_encode(scaled).reshape(Vm.shape)
+    return np.moveaxis(codes, -1, axis), np.moveaxis((xexp + 127).astype(np.uint8), -1, axis)
+
+
+def dequantize_mx(codes: np.ndarray, scale_bytes: np.ndarray, axis: int) -> np.ndarray:
+    """value(code) * 2^(scale byte - 127), blocks of 32 along ``axis``, float64."""
+    vals = e4m3_values()[np.asarray(codes).astype(np.int64)]
+    x = np.repeat(np.ldexp(1.0, scale_bytes.astype(np.int64) - 127), MX_BLOCK, axis=axis)
+    return vals * x
+
+
+def expert_ffn_mx(rows: np.ndarray, W1e: np.ndarray, W2e: np.ndarray) -> np.ndarray:
+    """One expert on MX-quantised operands: rows (already dequantised MX
+    activations) @ W1e (dequantised), SiLU, the result re-quantised to MX along
+    its F axis (the W2 product's reduction axis) and dequantised, @ W2e."""
+    h = silu(rows @ W1e)
+    hq, hs = quantize_mx(h, axis=1)
+    return dequantize_mx(hq, hs, axis=1) @ W2e
 
 
 # ------------------------------------------------- capacity-limited routing --
@@ -430,23 +490,29 @@ def forward(x, Wr, b, W1: ArrayOrGetter, W2: ArrayOrGetter, k: int, drop_thresh:
 
 
 def forward_tokens(tokens: Sequence[int], x, Wr, b, W1: ArrayOrGetter, W2: ArrayOrGetter, k: int,
-                   drop_thresh: float = 0.0, W1s=None, W2s=None):
+                   drop_thresh: float = 0.0, W1s=None, W2s=None, mx: bool = False):
     """Layer output for selected tokens only, by the layer equation.
 
     [P3] "MoE层的结构与token路由": y(x) is the sum over the selected experts
     of w_e(x) * E_e(x). Returns (ids, w, keep, y) for ``tokens``. Each
     expert's weights are fetched once and applied to the sampled tokens that
     chose it; the per-token sum then runs in slot order.
+
+    mx=True: the MX fp8 layer -- routing on x as given, the experts on the
+    token rows quantised to MX along H (before dispatch) and dequantised, with
+    expert_ffn_mx (W1, W2 are then the dequantised MX weights).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     xs = np.asarray(x, dtype=np.float64)[tokens]
     r = route(xs, Wr, b, k, drop_thresh)
     n = len(tokens)
     H = xs.shape[1]
+    xe = dequantize_mx(*quantize_mx(xs, axis=1), axis=1) if mx else xs
+    ffn = expert_ffn_mx if mx else expert_ffn
     contrib = np.zeros((n, k, H), dtype=np.float64)
     for e in np.unique(r.ids[r.keep]):
         which = np.argwhere((r.ids == e) & r.keep)
-        ye = expert_ffn(xs[which[:, 0]], _w(W1, int(e)), _w(W2, int(e)))
+        ye = ffn(xe[which[:, 0]], _w(W1, int(e)), _w(W2, int(e)))
         contrib[which[:, 0], which[:, 1]] = ye
     y = np.zeros((n, H), dtype=np.float64)
     for j in range(k):
