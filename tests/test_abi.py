@@ -210,6 +210,38 @@ def test_fp8_rejects(lib):
     assert lib.moe_forward_fp8(*bad) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_mxfp8_rejects(lib):
+    N = None
+    bf16 = 1
+    assert lib.moe_mxfp8_weight_bytes(128, 2048, 768) == 128 * 768 * 2048
+    assert lib.moe_mxfp8_scale_bytes(128, 2048, 768) == 128 * 16 * 768 * 4
+    assert lib.moe_mxfp8_weight_bytes(2, 64, 128) == 0                    # K % 128 != 0
+    assert lib.moe_mxfp8_scale_bytes(2, 128, 100) == 2 * 1 * 128 * 4      # N padded to 128
+    assert lib.moe_quantize_mxfp8(_p(), 2, 64, 128, bf16, _p(), _p(), N) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp8(_p(), 2, 128, 128, 9, _p(), _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8(_p(), 2, 128, 128, bf16, _p(), N, N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8_rows(_p(), 4, 96, bf16, _p(), _p(), N) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp8_rows(_p(), 0, 128, bf16, _p(), _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp8_workspace_bytes(64, 256, 256, 4, 2) > 0
+    assert lib.moe_mxfp8_workspace_bytes(64, 192, 256, 4, 2) == 0          # H % 128 != 0
+    assert lib.moe_mxfp8_workspace_bytes(64, 256, 128, 4, 2) == 0          # F < 256
+    need = lib.moe_mxfp8_workspace_bytes(64, 256, 256, 4, 2)
+    args = [_p(), _p(), N, _p(), _p(), _p(), _p(), 64, 256, 256, 4, 2, 0.0, _p(), 0, N, N, N, N, _p(), need, N]
+    assert len(args) == len(lib.moe_forward_mxfp8.argtypes)
+    bad = list(args)
+    bad[20] = need - 1
+    assert lib.moe_forward_mxfp8(*bad) == moe.MOE_ERR_WORKSPACE
+    bad = list(args)
+    bad[6] = N
+    assert lib.moe_forward_mxfp8(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[8] = 320
+    assert lib.moe_forward_mxfp8(*bad) == moe.MOE_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[14] = 4
+    assert lib.moe_forward_mxfp8(*bad) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(ImportError):
         moe.load_library(str(tmp_path / "missing.so"))

@@ -23,7 +23,9 @@ EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_work
            "moe_combine", "moe_forward", "moe_route_capacity_workspace_bytes", "moe_route_capacity",
            "moe_select_capacity_workspace_bytes", "moe_select_capacity", "moe_pad_dispatch",
            "moe_grouped_ffn_padded_workspace_bytes", "moe_grouped_ffn_padded", "moe_fp8_weight_bytes",
-           "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_forward_fp8")
+           "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_forward_fp8", "moe_mxfp8_weight_bytes",
+           "moe_mxfp8_scale_bytes", "moe_quantize_mxfp8", "moe_quantize_mxfp8_rows", "moe_mxfp8_workspace_bytes", "moe_grouped_ffn_mxfp8",
+           "moe_forward_mxfp8")
 
 
 class MoEError(RuntimeError):
@@ -92,6 +94,21 @@ def load_library(path: Optional[str] = None):
     lib.moe_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, vp, vp,
                                     vp, sz, vp]
     lib.moe_forward_fp8.restype = i32
+    lib.moe_mxfp8_weight_bytes.argtypes = [i32, i32, i32]
+    lib.moe_mxfp8_weight_bytes.restype = sz
+    lib.moe_mxfp8_scale_bytes.argtypes = [i32, i32, i32]
+    lib.moe_mxfp8_scale_bytes.restype = sz
+    lib.moe_quantize_mxfp8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_quantize_mxfp8.restype = i32
+    lib.moe_quantize_mxfp8_rows.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_quantize_mxfp8_rows.restype = i32
+    lib.moe_mxfp8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.moe_mxfp8_workspace_bytes.restype = sz
+    lib.moe_grouped_ffn_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.moe_grouped_ffn_mxfp8.restype = i32
+    lib.moe_forward_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, vp,
+                                      vp, vp, sz, vp]
+    lib.moe_forward_mxfp8.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -351,3 +368,66 @@ def moe_forward_fp8(x, Wr, bias, W1q, W1_scale, W2q, W2_scale, k: int, drop_thre
                                         ws.numel(), _stream(stream))
     _check(st, "moe_forward_fp8")
     return y
+
+
+def moe_quantize_mxfp8(W, Wq=None, W_scale=None, stream=None):
+    """MX fp8 codes of W [E,K,N] (blocks of 32 along K) in the tiled layout of
+    include/moe.h, and their scale bytes. Returns (Wq uint8, W_scale uint8)."""
+    E, K, N = W.shape
+    lib = load_library()
+    nq, ns = int(lib.moe_mxfp8_weight_bytes(E, K, N)), int(lib.moe_mxfp8_scale_bytes(E, K, N))
+    if nq == 0:
+        _check(MOE_ERR_UNSUPPORTED, "moe_mxfp8_weight_bytes")
+    Wq = torch.empty(nq, dtype=torch.uint8, device=W.device) if Wq is None else Wq
+    W_scale = torch.empty(ns, dtype=torch.uint8, device=W.device) if W_scale is None else W_scale
+    st = lib.moe_quantize_mxfp8(_ptr(W), E, K, N, _dt(W), _ptr(Wq), _ptr(W_scale), _stream(stream))
+    _check(st, "moe_quantize_mxfp8")
+    return Wq, W_scale
+
+
+def moe_quantize_mxfp8_rows(x, xq=None, x_scale=None, stream=None):
+    """MX fp8 codes of the rows of x [T,H] (blocks of 32 along H): xq [T,H] uint8 and the
+    scale bytes [H/128, T, 4] uint8."""
+    T, H = x.shape
+    xq = torch.empty((T, H), dtype=torch.uint8, device=x.device) if xq is None else xq
+    x_scale = torch.empty((H // 128, T, 4), dtype=torch.uint8, device=x.device) if x_scale is None else x_scale
+    st = load_library().moe_quantize_mxfp8_rows(_ptr(x), T, H, _dt(x), _ptr(xq), _ptr(x_scale), _stream(stream))
+    _check(st, "moe_quantize_mxfp8_rows")
+    return xq, x_scale
+
+
+def moe_forward_mxfp8(x, Wr, bias, W1q, W1_scale, W2q, W2_scale, F: int, k: int, drop_thresh: float = 0.0,
+                      E: Optional[int] = None, out_dtype=torch.float32, y=None, topk_ids=None, topk_w=None,
+                      expert_offsets=None, inv=None, ws=None, stream=None):
+    """The whole layer with MX fp8 experts (x, Wr bf16). Returns y [T,H]."""
+    T, H = x.shape
+    E = Wr.shape[1] if E is None else E
+    dev = x.device
+    lib = load_library()
+    y = torch.empty((T, H), dtype=out_dtype, device=dev) if y is None else y
+    need = int(lib.moe_mxfp8_workspace_bytes(T, H, F, E, k))
+    if need == 0:
+        _check(MOE_ERR_UNSUPPORTED, "moe_mxfp8_workspace_bytes")
+    ws = _ws(need, dev) if ws is None else ws
+    st = lib.moe_forward_mxfp8(_ptr(x), _ptr(Wr), _ptr(bias), _ptr(W1q), _ptr(W1_scale), _ptr(W2q), _ptr(W2_scale), T,
+                               H, F, E, k, float(drop_thresh), _ptr(y), _dt(y), _ptr(topk_ids), _ptr(topk_w),
+                               _ptr(expert_offsets), _ptr(inv), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_forward_mxfp8")
+    return y
+
+
+def moe_grouped_ffn_mxfp8(xq, x_scale, row_token, expert_offsets, W1q, W1_scale, W2q, W2_scale, H: int, F: int,
+                          k: int, h_codes=None, h_scale=None, y_perm=None, stream=None):
+    """Both expert products on MX operands. Returns (h_codes [T*k,F] uint8, h_scale [F/128,T*k,4] uint8,
+    y_perm [T*k,H] fp32)."""
+    T = xq.shape[0]
+    E = expert_offsets.shape[0] - 1
+    dev = xq.device
+    h_codes = torch.empty((T * k, F), dtype=torch.uint8, device=dev) if h_codes is None else h_codes
+    h_scale = torch.empty((F // 128, T * k, 4), dtype=torch.uint8, device=dev) if h_scale is None else h_scale
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
+    st = load_library().moe_grouped_ffn_mxfp8(_ptr(xq), _ptr(x_scale), _ptr(row_token), _ptr(expert_offsets), _ptr(W1q),
+                                              _ptr(W1_scale), _ptr(W2q), _ptr(W2_scale), T, H, F, E, k, _ptr(h_codes),
+                                              _ptr(h_scale), _ptr(y_perm), _stream(stream))
+    _check(st, "moe_grouped_ffn_mxfp8")
+    return h_codes, h_scale, y_perm

@@ -14,6 +14,7 @@
 // function of the float32 values alone. Codes are stored as 8 KiB tiles of
 // 128 columns x 64 k (see f8_swz in gemm_dma.hpp): per expert
 // [ceil(N/128)][K/64][128][64] bytes, columns past N holding code 0.
+#include "fp8_codes.hpp"
 #include "gemm_dma.hpp"
 #include "moe_internal.hpp"
 
@@ -27,25 +28,6 @@ using dma::kF8TileN;
 
 __device__ __forceinline__ float load_f32(const float* p) { return *p; }
 __device__ __forceinline__ float load_f32(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
-
-// float32 -> e4m3 code, round to nearest even, saturating at 448 (0x7E).
-// Below 2^-6 the e4m3 grid is uniform with step 2^-9, so the code is the
-// rounded multiple itself (a * 512 is exact); from 2^-6 up, rounding the
-// float32 significand to 3 bits (carry into the exponent included) and
-// rebiasing the exponent from 127 to 7 gives the code.
-__device__ __forceinline__ uint32_t e4m3_rne(float r) {
-    const uint32_t sign = (__float_as_uint(r) >> 24) & 0x80u;
-    const float a = fabsf(r);
-    uint32_t code;
-    if (a < 0x1p-6f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal, code 0x08
-    } else {
-        const uint32_t u = __float_as_uint(a);
-        const uint32_t rounded = u + 0x7FFFFu + ((u >> 20) & 1u);
-        code = min((rounded >> 20) - (120u << 3), 0x7Eu);
-    }
-    return code | sign;
-}
 
 // scales[e][n]; grid (ceil(N/64), E), 256 threads: 64 columns x 4 k-phases.
 template <typename TIn>

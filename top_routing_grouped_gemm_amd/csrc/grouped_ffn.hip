@@ -27,6 +27,7 @@
 #include <limits.h>
 
 #include "gemm_dma.hpp"
+#include "gemm_mx.hpp"
 #include "mfma_tiles.hpp"
 #include "moe_internal.hpp"
 
@@ -310,6 +311,26 @@ hipError_t run_fp8_cfg(TileCfg cfg, const void* A, long lda, const int32_t* a_ro
                                    s);
 }
 
+// MX fp8 shape (gemm_mx_kernel): 256 x 256 tiles, 128-k stages of 66 KB
+// (codes of A and B plus their scale dwords), a 2-stage ring, 8 waves.
+struct MxLarge {
+    static constexpr int BM = 256, BN = 256, NS = 2, WM = 4, WN = 2;
+};
+
+template <class C, int EPI>
+hipError_t run_mx(const void* A, long lda, const int32_t* a_rows, const void* a_sc, long a_sc_kstride, const void* B,
+                  long strideB, const void* b_sc, long b_sc_estride, int Npad, void* Cm, long ldc, long c_cap,
+                  void* c_sc, const int32_t* offsets, int E, int max_rows, int N, int K, hipStream_t s) {
+    const int n_tiles = (N + C::BN - 1) / C::BN;
+    const long grid = max_mtiles(C::BM, offsets, E, 0, max_rows) * n_tiles + dma::kXcds;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dma::gemm_mx_kernel<C::BM, C::BN, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
+                       dim3(C::WM * C::WN * 64), 0, s, (const uint8_t*)A, lda, a_rows, (const uint8_t*)a_sc,
+                       a_sc_kstride, (const uint8_t*)B, strideB, (const uint8_t*)b_sc, b_sc_estride, Npad, Cm, ldc,
+                       c_cap, (uint8_t*)c_sc, offsets, E, 0, INT_MAX, N, K, n_tiles);
+    return hipGetLastError();
+}
+
 template <class C>
 bool dma_ok(long lda, long ldb, int N, int K) {
     return K % C::BK == 0 && K >= 2 * C::BK && N % 8 == 0 && N >= 8 && lda % 8 == 0 && ldb % 8 == 0;
@@ -447,6 +468,27 @@ hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int
         return run_fp8_cfg<kEpiPacked24>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, cap, offsets, E, max_rows, H, F,
                                          s);
     return run_fp8_cfg<kEpiF32Out>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, 0, offsets, E, max_rows, H, F, s);
+}
+
+bool ffn_mx_ok(int H, int F) { return H % 128 == 0 && F % 128 == 0 && H >= 256 && F >= 256; }
+
+hipError_t launch_ffn_up_mx(const void* xq, const void* xs, int T, const int32_t* row_token, const int32_t* offsets,
+                            int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H, int F, void* hq,
+                            void* hs, long cap, hipStream_t s) {
+    return run_mx<MxLarge, 3>(xq, H, row_token, xs, (long)T * 4, W1q, mx_weight_bytes(1, H, F), W1s,
+                              mx_weight_scale_bytes(1, H, F), F, hq, F, cap, hs, offsets, E, max_rows, F, H, s);
+}
+
+hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const int32_t* offsets, int E, int max_rows,
+                              const uint8_t* W2q, const uint8_t* W2s, int F, int H, bool packed, void* y,
+                              hipStream_t s) {
+    if (packed)
+        return run_mx<MxLarge, kEpiPacked24>(hq, F, nullptr, hs, cap * 4, W2q, mx_weight_bytes(1, F, H), W2s,
+                                             mx_weight_scale_bytes(1, F, H), H, y, H, cap, nullptr, offsets, E,
+                                             max_rows, H, F, s);
+    return run_mx<MxLarge, kEpiF32Out>(hq, F, nullptr, hs, cap * 4, W2q, mx_weight_bytes(1, F, H), W2s,
+                                       mx_weight_scale_bytes(1, F, H), H, y, H, 0, nullptr, offsets, E, max_rows, H,
+                                       F, s);
 }
 
 TileCfg choose_tile(long rows, int groups) {

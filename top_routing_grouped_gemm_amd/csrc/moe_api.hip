@@ -89,6 +89,36 @@ FwdLayout fwd_layout(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) 
     return L;
 }
 
+// Workspace of moe_forward_mxfp8: routing and dispatch maps as in moe_forward,
+// the MX codes and scales of x and of the SiLU output, and the 24-bit planes of y_perm.
+struct MxLayout {
+    size_t ids, w, offsets, inv, row_token, partial, route, xq, xs, hq, hs, y, total;
+};
+
+MxLayout mx_layout(int T, int H, int F, int E, int k) {
+    MxLayout L;
+    const size_t TK = (size_t)T * k;
+    size_t off = 0;
+    auto take = [&](size_t& field, size_t bytes) {
+        field = off;
+        off = align_up(off + bytes);
+    };
+    take(L.ids, TK * sizeof(int32_t));
+    take(L.w, TK * sizeof(float));
+    take(L.offsets, (size_t)(E + 1) * sizeof(int32_t));
+    take(L.inv, TK * sizeof(int32_t));
+    take(L.row_token, TK * sizeof(int32_t));
+    take(L.partial, permute_bytes(T, E, k));
+    take(L.route, moe::route_workspace_bytes(T, H, E, moe::kBF16));
+    take(L.xq, (size_t)T * H);
+    take(L.xs, (size_t)(H / 128) * T * 4);
+    take(L.hq, TK * F);
+    take(L.hs, (size_t)(F / 128) * TK * 4);
+    take(L.y, TK * H * 3);
+    L.total = off;
+    return L;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 #define MOE_TRY(expr)                          \
@@ -453,6 +483,96 @@ int moe_forward_fp8(const void* x, const void* Wr, const float* bias, const uint
     MOE_TRY(moe::launch_ffn_down_fp8(h, off, E, rows, W2q, W2_scale, F, H, cfg, true, y_planes, rows, stream));
     return hip_status(moe::launch_combine_packed(y_planes, rows, iv, w, nullptr, T, H, k, (moe::Dtype)out_dt, y,
                                                  stream));
+}
+
+size_t moe_mxfp8_weight_bytes(int E, int K, int N) {
+    if (E < 1 || K < 1 || N < 1 || E > kMaxExperts || K % 128 != 0) return 0;
+    return (size_t)moe::mx_weight_bytes(E, K, N);
+}
+
+size_t moe_mxfp8_scale_bytes(int E, int K, int N) {
+    if (E < 1 || K < 1 || N < 1 || E > kMaxExperts || K % 128 != 0) return 0;
+    return (size_t)moe::mx_weight_scale_bytes(E, K, N);
+}
+
+int moe_quantize_mxfp8(const void* W, int E, int K, int N, moe_dtype_t dt, uint8_t* Wq, uint8_t* W_scale,
+                       hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    if (E < 1 || K < 1 || N < 1) return MOE_ERR_INVALID_ARG;
+    if (E > kMaxExperts || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((long long)E * ((N + 127) / 128) * (K / 128) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!W || !Wq || !W_scale) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_quantize_mx_weights(W, E, K, N, (Dtype)dt, Wq, W_scale, stream));
+}
+
+int moe_quantize_mxfp8_rows(const void* x, int T, int H, moe_dtype_t dt, uint8_t* xq, uint8_t* x_scale,
+                            hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    if (T < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+    if (H % 128 != 0 || (long long)T * H / 4 >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+    if (!x || !xq || !x_scale) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_quantize_mx_rows(x, T, H, (Dtype)dt, xq, x_scale, stream));
+}
+
+int moe_grouped_ffn_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const int32_t* row_token,
+                          const int32_t* expert_offsets, const uint8_t* W1q, const uint8_t* W1_scale,
+                          const uint8_t* W2q, const uint8_t* W2_scale, int T, int H, int F, int E, int k,
+                          uint8_t* h_codes, uint8_t* h_scale, float* y_perm, hipStream_t stream) {
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if (!moe::ffn_mx_ok(H, F)) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k * F >= (1LL << 31) || (long long)T * k * H * 4 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!xq || !x_scale || !row_token || !expert_offsets || !W1q || !W1_scale || !W2q || !W2_scale || !h_codes ||
+        !h_scale || !y_perm)
+        return MOE_ERR_INVALID_ARG;
+    const long rows = (long)T * k;
+    MOE_TRY(moe::launch_ffn_up_mx(xq, x_scale, T, row_token, expert_offsets, E, (int)rows, W1q, W1_scale, H, F,
+                                  h_codes, h_scale, rows, stream));
+    return hip_status(moe::launch_ffn_down_mx(h_codes, h_scale, rows, expert_offsets, E, (int)rows, W2q, W2_scale, F,
+                                              H, false, y_perm, stream));
+}
+
+size_t moe_mxfp8_workspace_bytes(int T, int H, int F, int E, int k) {
+    if (check_sizes(T, H, F, E, k) != MOE_OK || F < 1 || !moe::ffn_mx_ok(H, F)) return 0;
+    return mx_layout(T, H, F, E, k).total;
+}
+
+int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const uint8_t* W1q, const uint8_t* W1_scale,
+                      const uint8_t* W2q, const uint8_t* W2_scale, int T, int H, int F, int E, int k,
+                      float drop_thresh, void* y, moe_dtype_t out_dt, int32_t* topk_ids, float* topk_w,
+                      int32_t* expert_offsets, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if (!moe::ffn_mx_ok(H, F)) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k * F >= (1LL << 31) || (long long)T * k * H * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!x || !Wr || !W1q || !W1_scale || !W2q || !W2_scale || !y || !ws) return MOE_ERR_INVALID_ARG;
+    const MxLayout L = mx_layout(T, H, F, E, k);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + L.ids);
+    float* w = topk_w ? topk_w : (float*)(base + L.w);
+    int32_t* off = expert_offsets ? expert_offsets : (int32_t*)(base + L.offsets);
+    int32_t* iv = inv ? inv : (int32_t*)(base + L.inv);
+    int32_t* row_token = (int32_t*)(base + L.row_token);
+    const long rows = (long)T * k;
+    uint8_t* xq = (uint8_t*)(base + L.xq);
+    uint8_t* xs = (uint8_t*)(base + L.xs);
+    // the router keeps bf16 x; the experts read x quantised to MX before dispatch (gathered by the W1 launch)
+    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, moe::kBF16, ids, w, base + L.route, stream));
+    if ((st = enqueue_permute(x, ids, w, T, H, E, k, MOE_BF16, nullptr, off, row_token, iv,
+                              (int32_t*)(base + L.partial), false, stream)) != MOE_OK)
+        return st;
+    MOE_TRY(moe::launch_quantize_mx_rows(x, T, H, moe::kBF16, xq, xs, stream));
+    MOE_TRY(moe::launch_ffn_up_mx(xq, xs, T, row_token, off, E, (int)rows, W1q, W1_scale, H, F, base + L.hq,
+                                  base + L.hs, rows, stream));
+    MOE_TRY(moe::launch_ffn_down_mx(base + L.hq, base + L.hs, rows, off, E, (int)rows, W2q, W2_scale, F, H, true,
+                                    base + L.y, stream));
+    return hip_status(
+        moe::launch_combine_packed(base + L.y, rows, iv, w, nullptr, T, H, k, (moe::Dtype)out_dt, y, stream));
 }
 
 }  // extern "C"

@@ -95,6 +95,25 @@ hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int
                                const float* s2, int F, int H, TileCfg cfg, bool packed, void* y, long cap,
                                hipStream_t s);
 
+// MX fp8 (mx_quant.hip, gemm_mx.hpp): token rows quantised before dispatch to
+// codes xq[T][H] + scales xs[H/128][T][4]; expert weights [E][K][N] to code
+// tiles (mx_weight_bytes) + scales (mx_weight_scale_bytes). The W1 launch
+// gathers xq rows through row_token and writes SiLU(h) as MX codes hq[cap][F]
+// + scales hs[F/128][cap][4]; the W2 launch writes y as fp32 [cap][H] or the
+// 24-bit planes (packed). Needs H, F multiples of 128 and >= 256.
+long mx_weight_bytes(int E, int K, int N);
+long mx_weight_scale_bytes(int E, int K, int N);
+hipError_t launch_quantize_mx_rows(const void* x, int T, int H, Dtype dt, uint8_t* xq, uint8_t* xs, hipStream_t s);
+hipError_t launch_quantize_mx_weights(const void* W, int E, int K, int N, Dtype dt, uint8_t* Wq, uint8_t* Ws,
+                                      hipStream_t s);
+bool ffn_mx_ok(int H, int F);
+hipError_t launch_ffn_up_mx(const void* xq, const void* xs, int T, const int32_t* row_token, const int32_t* offsets,
+                            int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H, int F, void* hq,
+                            void* hs, long cap, hipStream_t s);
+hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const int32_t* offsets, int E, int max_rows,
+                              const uint8_t* W2q, const uint8_t* W2s, int F, int H, bool packed, void* y,
+                              hipStream_t s);
+
 // y_perm given as the two planes of ffn_down_packs (cap = row capacity).
 hipError_t launch_combine_packed(const void* y_planes, long cap, const int32_t* inv, const float* w,
                                  const float* y_shared, int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
