@@ -310,6 +310,61 @@ def fp8_times(name, steps=20, reps=20):
                                    "bf16": round(flops / (ffn16 * 1e-3) / 1e12, 1)}}
 
 
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+
+
+def mx_times(name, steps=20, reps=20):
+    """MX fp8 experts (tokens and weights in OCP MX E4M3, products on the fp8 matrix cores) next to bf16 on one
+    workload: the layer (moe_forward_mxfp8 against moe_forward, no shared expert) and the two expert products
+    (moe_grouped_ffn_mxfp8 against moe_grouped_ffn), HIP events; fp8 MFMA fraction against 5.0 PFLOP/s."""
+    import torch
+
+    import gen
+    import top_routing_grouped_gemm_amd as moe
+
+    dev = torch.device("cuda:0")
+    I = gen.make_inputs(name)
+    d = gen.to_device(I, dev)
+    s = torch.cuda.current_stream()
+    T, H, F, E, k = I.T, I.H, I.F, I.E, I.k
+    lib = moe.load_library()
+    W1q, W1s = moe.moe_quantize_mxfp8(d["W1"])
+    W2q, W2s = moe.moe_quantize_mxfp8(d["W2"])
+    t_quant = event_time_ms(lambda: (moe.moe_quantize_mxfp8(d["W1"], Wq=W1q, W_scale=W1s),
+                                     moe.moe_quantize_mxfp8(d["W2"], Wq=W2q, W_scale=W2s)), 3, s)
+    wsm = torch.empty(lib.moe_mxfp8_workspace_bytes(T, H, F, E, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(moe.moe_workspace_bytes(T, H, F, E, k, 0, torch.bfloat16), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    fwd_mx = event_time_ms(lambda: moe.moe_forward_mxfp8(d["x"], d["Wr"], d["bias"], W1q, W1s, W2q, W2s, F, k, I.drop,
+                                                         y=y, ws=wsm), steps, s)
+    fwd16 = event_time_ms(lambda: moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], k, I.drop, y=y,
+                                                  ws=ws), steps, s)
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop)
+    x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, E)
+    xq, xs = moe.moe_quantize_mxfp8_rows(d["x"])
+    t_rows = event_time_ms(lambda: moe.moe_quantize_mxfp8_rows(d["x"], xq=xq, x_scale=xs), reps, s)
+    hq = torch.empty((T * k, F), dtype=torch.uint8, device=dev)
+    hs = torch.empty((F // 128, T * k, 4), dtype=torch.uint8, device=dev)
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    ffn_mx = event_time_ms(lambda: moe.moe_grouped_ffn_mxfp8(xq, xs, row_token, off, W1q, W1s, W2q, W2s, H, F, k,
+                                                             h_codes=hq, h_scale=hs, y_perm=y_perm), reps, s)
+    fws = torch.empty(moe.moe_ffn_workspace_bytes(T, F, E, k, 0, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ffn16 = event_time_ms(lambda: moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm, ws=fws),
+                          reps, s)
+    torch.cuda.synchronize()
+    A = int(off[-1].item())
+    flops = 4.0 * A * H * F
+    return {"workload": name, "T": T, "H": H, "F": F, "E": E, "k": k, "A": A,
+            "quantize_weights_ms_once": round(t_quant, 3), "quantize_rows_ms": round(t_rows, 5),
+            "forward_ms": {"mxfp8": round(fwd_mx, 5), "bf16": round(fwd16, 5)},
+            "tokens_per_s": {"mxfp8": round(T / (fwd_mx * 1e-3), 1), "bf16": round(T / (fwd16 * 1e-3), 1)},
+            "grouped_ffn_ms": {"mxfp8": round(ffn_mx, 5), "bf16": round(ffn16, 5)},
+            "grouped_ffn_tflops": {"mxfp8": round(flops / (ffn_mx * 1e-3) / 1e12, 1),
+                                   "bf16": round(flops / (ffn16 * 1e-3) / 1e12, 1)},
+            "grouped_ffn_peak_frac": {"mxfp8_vs_fp8_peak": round(flops / (ffn_mx * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                      "bf16_vs_bf16_peak": round(flops / (ffn16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+
+
 def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
     """The fp64 oracle, as it stands, on the host cores: whole prefill batches, repeated until about 10 s."""
     import numpy as np
@@ -354,6 +409,8 @@ def main():
                     help="with --only: time capacity-limited routing (this factor) against plain routing")
     ap.add_argument("--padded", action="store_true",
                     help="with --only: time the padded fixed-shape layout against the ragged grouped FFN")
+    ap.add_argument("--mx", action="store_true",
+                    help="with --only: time MX fp8 experts (fp8 matrix cores) against bf16 (layer and grouped FFN)")
     ap.add_argument("--fp8", action="store_true",
                     help="with --only: time fp8 expert weights against bf16 (layer and grouped FFN)")
     args = ap.parse_args()
@@ -380,6 +437,9 @@ def main():
         return
     if args.only and args.padded:
         print(json.dumps(padded_times(args.only)), flush=True)
+        return
+    if args.only and args.mx:
+        print(json.dumps(mx_times(args.only)), flush=True)
         return
     if args.only and args.fp8:
         print(json.dumps(fp8_times(args.only)), flush=True)
