@@ -315,8 +315,9 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 
 def mx_times(name, steps=20, reps=20):
     """MX fp8 experts (tokens and weights in OCP MX E4M3, products on the fp8 matrix cores) next to bf16 on one
-    workload: the layer (moe_forward_mxfp8 against moe_forward, no shared expert) and the two expert products
-    (moe_grouped_ffn_mxfp8 against moe_grouped_ffn), HIP events; fp8 MFMA fraction against 5.0 PFLOP/s."""
+    workload: the layer (moe_forward_mxfp8 against moe_forward, no shared expert) and the expert products
+    (moe_grouped_ffn_mxfp8, which includes quantising the dispatched rows, against moe_grouped_ffn), HIP events;
+    fp8 MFMA fraction against 5.0 PFLOP/s."""
     import torch
 
     import gen
@@ -343,11 +344,12 @@ def mx_times(name, steps=20, reps=20):
     x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, E)
     xq, xs = moe.moe_quantize_mxfp8_rows(d["x"])
     t_rows = event_time_ms(lambda: moe.moe_quantize_mxfp8_rows(d["x"], xq=xq, x_scale=xs), reps, s)
-    hq = torch.empty((T * k, F), dtype=torch.uint8, device=dev)
+    hq = torch.empty((F // 64, T * k, 64), dtype=torch.uint8, device=dev)
     hs = torch.empty((F // 128, T * k, 4), dtype=torch.uint8, device=dev)
     y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    ffn_mx = event_time_ms(lambda: moe.moe_grouped_ffn_mxfp8(xq, xs, row_token, off, W1q, W1s, W2q, W2s, H, F, k,
-                                                             h_codes=hq, h_scale=hs, y_perm=y_perm), reps, s)
+    wsx = torch.empty(lib.moe_grouped_ffn_mxfp8_workspace_bytes(T, H, k), dtype=torch.uint8, device=dev)
+    ffn_mx = event_time_ms(lambda: moe.moe_grouped_ffn_mxfp8(d["x"], row_token, off, W1q, W1s, W2q, W2s, F, k,
+                                                             h_codes=hq, h_scale=hs, y_perm=y_perm, ws=wsx), reps, s)
     fws = torch.empty(moe.moe_ffn_workspace_bytes(T, F, E, k, 0, torch.bfloat16), dtype=torch.uint8, device=dev)
     ffn16 = event_time_ms(lambda: moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm, ws=fws),
                           reps, s)

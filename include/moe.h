@@ -323,33 +323,38 @@ int moe_forward_fp8(const void* x, const void* Wr, const float* bias, const uint
  * at 448 (so values in [448, 512)X clamp to 448X). V / X is exact in fp32.
  *
  * Layouts (device memory, caller-owned):
- *   weights W [E][K][N] -> Wq (moe_mxfp8_weight_bytes): per expert, 16 KiB
- *     tiles of 128 columns x 128 k, tile (nb, kb) at ((e*NB + nb)*(K/128) + kb)*16384,
+ *   weights W [E][K][N] -> Wq (moe_mxfp8_weight_bytes): per expert, 8 KiB
+ *     tiles of 128 columns x 64 k, tile (nb, kb) at ((e*NB + nb)*(K/64) + kb)*8192,
  *     NB = ceil(N/128); inside a tile the code of (n, k) is at
- *     n*128 + ((k/16) ^ ((n >> 1) & 7))*16 + k%16.
+ *     n*64 + ((k/16) ^ (((n >> 1) & 3) ^ ((n >> 3) & 1)))*16 + k%16.
  *   weight scales (moe_mxfp8_scale_bytes): byte of (e, n, 32-k block b) at
  *     ((e*(K/128) + b/4)*NB*128 + n)*4 + b%4. Columns at or past N: code 0,
  *     scale byte 127.
  *   rows x [T][H] -> xq [T][H] bytes (row-major) and x_scale: byte of
  *     (t, 32-value block b) at ((b/4)*T + t)*4 + b%4.
+ *   h_codes (moe_grouped_ffn_mxfp8): k-blocked, code of (row r, column f) at
+ *     ((f/64)*T*k + r)*64 + f%64; h_scale: byte of (r, block b) at
+ *     ((b/4)*T*k + r)*4 + b%4.
  *
  * moe_quantize_mxfp8: K % 128 == 0 (else MOE_ERR_UNSUPPORTED); W1 [E,H,F]
  *   uses (K, N) = (H, F), W2 [E,F,H] uses (F, H).
  * moe_quantize_mxfp8_rows: H % 128 == 0.
  * moe_grouped_ffn_mxfp8: the two expert products on MX operands, step-wise:
- *   xq, x_scale from moe_quantize_mxfp8_rows; row_token, expert_offsets from
- *   moe_permute; writes h_codes [T*k][F] and h_scale (byte of (row r, block b)
- *   at ((b/4)*T*k + r)*4 + b%4): the MX codes of silu(x_row @ W1), and
- *   y_perm [T*k][H] fp32 = dequantised h @ W2. The matrix cores round inside
- *   each 64-k product block (measured: up to about 5e-5 of the sum of the
+ *   x [T,H] bf16 and row_token, expert_offsets from moe_permute; the token
+ *   rows are quantised once (moe_quantize_mxfp8_rows, into ws:
+ *   moe_grouped_ffn_mxfp8_workspace_bytes(T,H,k) bytes) and the first product
+ *   gathers their codes through row_token; writes h_codes,
+ *   h_scale (the MX codes of silu(x_row @ W1), layouts above) and y_perm
+ *   [T*k][H] fp32 = dequantised h @ W2. The matrix cores round inside each
+ *   64-k product block (measured: up to about 5e-5 of the sum of the
  *   products' magnitudes), so an h value within that distance of an E4M3
  *   rounding boundary may take the neighbouring code.
  * moe_forward_mxfp8: the layer with MX experts: the router on bf16 x (fp32
- *   logits) as in moe_forward; x quantised to MX; per expert
- *   y_e = mxq(silu(mxq(x) @ W1)) @ W2 with mxq the MX quantisation of its
- *   argument along the product's reduction axis and W1, W2 the MX weights;
- *   combine as moe_forward. x and Wr bf16; H and F multiples of 128 and
- *   >= 256; no shared expert. ws: moe_mxfp8_workspace_bytes(T,H,F,E,k).
+ *   logits) as in moe_forward; x quantised to MX before dispatch; per
+ *   expert y_e = mxq(silu(mxq(x) @ W1)) @ W2 with mxq the MX quantisation of
+ *   its argument along the product's reduction axis and W1, W2 the MX
+ *   weights; combine as moe_forward. x and Wr bf16; H and F multiples of 128;
+ *   no shared expert. ws: moe_mxfp8_workspace_bytes(T,H,F,E,k).
  */
 size_t moe_mxfp8_weight_bytes(int E, int K, int N);
 size_t moe_mxfp8_scale_bytes(int E, int K, int N);
@@ -357,10 +362,11 @@ int moe_quantize_mxfp8(const void* W, int E, int K, int N, moe_dtype_t dt, uint8
                        hipStream_t stream);
 int moe_quantize_mxfp8_rows(const void* x, int T, int H, moe_dtype_t dt, uint8_t* xq, uint8_t* x_scale,
                             hipStream_t stream);
-int moe_grouped_ffn_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const int32_t* row_token,
-                          const int32_t* expert_offsets, const uint8_t* W1q, const uint8_t* W1_scale,
-                          const uint8_t* W2q, const uint8_t* W2_scale, int T, int H, int F, int E, int k,
-                          uint8_t* h_codes, uint8_t* h_scale, float* y_perm, hipStream_t stream);
+size_t moe_grouped_ffn_mxfp8_workspace_bytes(int T, int H, int k);
+int moe_grouped_ffn_mxfp8(const void* x, const int32_t* row_token, const int32_t* expert_offsets,
+                          const uint8_t* W1q, const uint8_t* W1_scale, const uint8_t* W2q,
+                          const uint8_t* W2_scale, int T, int H, int F, int E, int k, uint8_t* h_codes,
+                          uint8_t* h_scale, float* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_mxfp8_workspace_bytes(int T, int H, int F, int E, int k);
 int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const uint8_t* W1q,
                       const uint8_t* W1_scale, const uint8_t* W2q, const uint8_t* W2_scale, int T, int H,

@@ -224,7 +224,9 @@ def test_mxfp8_rejects(lib):
     assert lib.moe_quantize_mxfp8_rows(_p(), 0, 128, bf16, _p(), _p(), N) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp8_workspace_bytes(64, 256, 256, 4, 2) > 0
     assert lib.moe_mxfp8_workspace_bytes(64, 192, 256, 4, 2) == 0          # H % 128 != 0
-    assert lib.moe_mxfp8_workspace_bytes(64, 256, 128, 4, 2) == 0          # F < 256
+    assert lib.moe_mxfp8_workspace_bytes(64, 256, 192, 4, 2) == 0          # F % 128 != 0
+    assert lib.moe_grouped_ffn_mxfp8_workspace_bytes(64, 256, 2) == 64 * 256 + 2 * 64 * 4
+    assert lib.moe_grouped_ffn_mxfp8_workspace_bytes(64, 192, 2) == 0
     need = lib.moe_mxfp8_workspace_bytes(64, 256, 256, 4, 2)
     args = [_p(), _p(), N, _p(), _p(), _p(), _p(), 64, 256, 256, 4, 2, 0.0, _p(), 0, N, N, N, N, _p(), need, N]
     assert len(args) == len(lib.moe_forward_mxfp8.argtypes)

@@ -50,11 +50,12 @@ def _bits(a):
 
 
 def unpack_weight_codes(buf, E, K, N):
-    """[E][NB][K/128][128 n][128 k] tiles, 16-byte chunk c of column n at c ^ ((n >> 1) & 7) -> [E][K][N]."""
-    NB, KB = (N + 127) // 128, K // 128
-    t = np.asarray(buf, dtype=np.uint8).reshape(E, NB, KB, 128, 8, 16)
+    """[E][NB][K/64][128 n][64 k] tiles, 16-byte chunk c of column n at
+    c ^ (((n >> 1) & 3) ^ ((n >> 3) & 1)) -> [E][K][N] and the padding columns."""
+    NB, KB = (N + 127) // 128, K // 64
+    t = np.asarray(buf, dtype=np.uint8).reshape(E, NB, KB, 128, 4, 16)
     n = np.arange(128)
-    where = np.arange(8)[None, :] ^ ((n >> 1) & 7)[:, None]
+    where = np.arange(4)[None, :] ^ (((n >> 1) & 3) ^ ((n >> 3) & 1))[:, None]
     t = np.take_along_axis(t, where[None, None, None, :, :, None], axis=4)
     codes = t.transpose(0, 2, 4, 5, 1, 3).reshape(E, K, NB * 128)
     return codes[:, :, :N], codes[:, :, N:]
@@ -165,8 +166,7 @@ def _validate_layer(dev, I, tokens=None):
     W2q, W2s = moe.moe_quantize_mxfp8(d["W2"])
     ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], I.k, I.drop)
     _, off, row_token, inv = moe.moe_permute(d["x"], ids, w, I.E)
-    xq, xs = moe.moe_quantize_mxfp8_rows(d["x"])
-    hq, hs, y_perm = moe.moe_grouped_ffn_mxfp8(xq, xs, row_token, off, W1q, W1s, W2q, W2s, I.H, I.F, I.k)
+    hq, hs, y_perm = moe.moe_grouped_ffn_mxfp8(d["x"], row_token, off, W1q, W1s, W2q, W2s, I.F, I.k)
     y_steps = moe.moe_combine(y_perm, inv, w)
     y = moe.moe_forward_mxfp8(d["x"], d["Wr"], d["bias"], W1q, W1s, W2q, W2s, I.F, I.k, I.drop)
     y2 = moe.moe_forward_mxfp8(d["x"], d["Wr"], d["bias"], W1q, W1s, W2q, W2s, I.F, I.k, I.drop)
@@ -185,7 +185,7 @@ def _validate_layer(dev, I, tokens=None):
     x = I.f64(I.x)
     xe = oracle.dequantize_mx(*oracle.quantize_mx(x[tokens], axis=1), axis=1)
     W1, W2 = _mx_getter(I.W1, I.f64), _mx_getter(I.W2, I.f64)
-    hq_n = hq.cpu().numpy()
+    hq_n = hq.cpu().numpy().transpose(1, 0, 2).reshape(I.T * I.k, I.F)  # k-blocked [F/64][rows][64] -> [rows][F]
     hs_n = hs.cpu().numpy().transpose(1, 0, 2).reshape(I.T * I.k, I.F // 32)
     yp_n = y_perm.double().cpu().numpy()
     pos = {int(t): i for i, t in enumerate(tokens)}

@@ -25,6 +25,7 @@ EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_work
            "moe_grouped_ffn_padded_workspace_bytes", "moe_grouped_ffn_padded", "moe_fp8_weight_bytes",
            "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_forward_fp8", "moe_mxfp8_weight_bytes",
            "moe_mxfp8_scale_bytes", "moe_quantize_mxfp8", "moe_quantize_mxfp8_rows", "moe_mxfp8_workspace_bytes", "moe_grouped_ffn_mxfp8",
+           "moe_grouped_ffn_mxfp8_workspace_bytes",
            "moe_forward_mxfp8")
 
 
@@ -104,7 +105,9 @@ def load_library(path: Optional[str] = None):
     lib.moe_quantize_mxfp8_rows.restype = i32
     lib.moe_mxfp8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.moe_mxfp8_workspace_bytes.restype = sz
-    lib.moe_grouped_ffn_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.moe_grouped_ffn_mxfp8_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_grouped_ffn_mxfp8_workspace_bytes.restype = sz
+    lib.moe_grouped_ffn_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_grouped_ffn_mxfp8.restype = i32
     lib.moe_forward_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, vp,
                                       vp, vp, sz, vp]
@@ -416,18 +419,21 @@ def moe_forward_mxfp8(x, Wr, bias, W1q, W1_scale, W2q, W2_scale, F: int, k: int,
     return y
 
 
-def moe_grouped_ffn_mxfp8(xq, x_scale, row_token, expert_offsets, W1q, W1_scale, W2q, W2_scale, H: int, F: int,
-                          k: int, h_codes=None, h_scale=None, y_perm=None, stream=None):
-    """Both expert products on MX operands. Returns (h_codes [T*k,F] uint8, h_scale [F/128,T*k,4] uint8,
-    y_perm [T*k,H] fp32)."""
-    T = xq.shape[0]
+def moe_grouped_ffn_mxfp8(x, row_token, expert_offsets, W1q, W1_scale, W2q, W2_scale, F: int, k: int, h_codes=None,
+                          h_scale=None, y_perm=None, ws=None, stream=None):
+    """Both expert products on MX operands from bf16 x and moe_permute's maps (the dispatched rows are quantised
+    as they are copied). Returns (h_codes [F/64, T*k, 64] uint8 (k-blocked), h_scale [F/128, T*k, 4] uint8,
+    y_perm [T*k, H] fp32)."""
+    T, H = x.shape
     E = expert_offsets.shape[0] - 1
-    dev = xq.device
-    h_codes = torch.empty((T * k, F), dtype=torch.uint8, device=dev) if h_codes is None else h_codes
+    dev = x.device
+    lib = load_library()
+    h_codes = torch.empty((F // 64, T * k, 64), dtype=torch.uint8, device=dev) if h_codes is None else h_codes
     h_scale = torch.empty((F // 128, T * k, 4), dtype=torch.uint8, device=dev) if h_scale is None else h_scale
     y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
-    st = load_library().moe_grouped_ffn_mxfp8(_ptr(xq), _ptr(x_scale), _ptr(row_token), _ptr(expert_offsets), _ptr(W1q),
-                                              _ptr(W1_scale), _ptr(W2q), _ptr(W2_scale), T, H, F, E, k, _ptr(h_codes),
-                                              _ptr(h_scale), _ptr(y_perm), _stream(stream))
+    ws = _ws(lib.moe_grouped_ffn_mxfp8_workspace_bytes(T, H, k), dev) if ws is None else ws
+    st = lib.moe_grouped_ffn_mxfp8(_ptr(x), _ptr(row_token), _ptr(expert_offsets), _ptr(W1q), _ptr(W1_scale),
+                                   _ptr(W2q), _ptr(W2_scale), T, H, F, E, k, _ptr(h_codes), _ptr(h_scale),
+                                   _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_grouped_ffn_mxfp8")
     return h_codes, h_scale, y_perm

@@ -10,20 +10,23 @@
 // passes applies to block l/32 of its row or column. Here lane half h holds k
 // = 16h..16h+15 of block 0 and 32+16h.. of block 1: two 16-byte runs.
 //
-// Stage layout (BK = 128 k): A [BM][128 B] with 16-byte chunk c of row r at
-// c ^ ((r >> 1) & 7), loaded from row-major codes (optionally gathered through
-// a_rows) with the inverse XOR applied to the source; B as whole 128 x 128
-// code tiles copied verbatim (the quantiser pre-applies the same XOR); then
-// one dword of 4 scale bytes (the stage's four 32-k blocks) per A row and per
-// B column, loaded with 4-byte direct-to-LDS loads so that rows gathered from
-// different tokens need no staging. Waves 0..BM/64-1 load the A scales, the
-// others the B scales: every wave issues the same number of loads per stage.
+// Stage layout (BK = 64 k, one MFMA slice): A [BM][64 B] and B [BN/128 tiles]
+// [128][64 B], both with 16-byte chunk c of row r at c ^ f(r), f(r) =
+// ((r >> 1) & 3) ^ ((r >> 3) & 1) (two 16-byte reads of 32 rows spread over
+// the banks for 16- and 32-lane phases). A rows come either gathered from
+// row-major token codes (64-byte pieces) or from a k-blocked code array
+// [K/64][cap][64] (a stage of rows is one contiguous run); the loader applies
+// the inverse XOR to the source. B tiles are copied verbatim (the quantiser
+// pre-applies the XOR). Then one dword of 4 scale bytes (the 128-k block pair the stage
+// belongs to) per A row and per B column, by 4-byte direct-to-LDS loads:
+// waves 0..BM/64-1 load the A rows, the others the B columns, so every wave
+// issues the same number of loads per stage. 34 KB stages, a 4-stage ring.
 //
 // Epilogue 3 re-quantises the SiLU output to MX along N (the next product's
 // reduction axis): per row, each 32-column block's maximum comes from a
-// 3-step xor shuffle after the quad transpose, the codes go to C[rows][N]
-// and the wave's four scale bytes (128 columns) to one dword of
-// c_sc[N/128][c_cap][4].
+// 3-step xor shuffle after the quad transpose; the codes go to the k-blocked
+// C[N/64][c_cap][64] the next launch reads as A, and the wave's four scale
+// bytes (128 columns) to one dword of c_sc[N/128][c_cap][4].
 #pragma once
 
 #include "fp8_codes.hpp"
@@ -32,9 +35,9 @@
 namespace moe {
 namespace dma {
 
-constexpr int kMxBK = 128;
-constexpr int kMxTileN = 128, kMxTileBytes = kMxTileN * kMxBK;  // 16 KiB weight code tiles
-__host__ __device__ __forceinline__ int mx_swz(int r) { return (r >> 1) & 7; }
+constexpr int kMxBK = 64;
+constexpr int kMxTileN = 128, kMxTileBytes = kMxTileN * kMxBK;  // 8 KiB weight code tiles
+__host__ __device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -46,13 +49,13 @@ __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
 }
 
 template <int TM, int TN, int WTM, int WTN>
-__device__ __forceinline__ void store_tile_mx(f32x16 (&acc)[TM][TN], uint8_t* C, long ldc, long c_cap,
+__device__ __forceinline__ void store_tile_mx(f32x16 (&acc)[TM][TN], uint8_t* C, long c_cap,
                                               uint8_t* c_sc, int rb, int re, int n0, int N, int wm, int wn) {
     static_assert(WTN == 128 && TN == 4, "a wave's 128 columns give one scale dword per row");
     const int l = lane_id();
     const int c0 = (l & 31) & ~3, m = l & 3;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(C + (long)rb * ldc, (short)0,
-                                                                        (int)((long)(re - rb) * ldc), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)((long)(N / kMxBK) * c_cap * kMxBK), 0x00020000);
     const __amdgpu_buffer_rsrc_t rsc =
         __builtin_amdgcn_make_buffer_rsrc(c_sc, (short)0, (int)((long)(N / kMxTileN) * c_cap * 4), 0x00020000);
     const int colw = n0 + wn * WTN;  // a multiple of 128
@@ -76,8 +79,8 @@ __device__ __forceinline__ void store_tile_mx(f32x16 (&acc)[TM][TN], uint8_t* C,
                 const int x = mx_exponent(am);
                 const uint32_t codes = mx_codes4(v[0], v[1], v[2], v[3], x);
                 const int col = colw + jj * 32 + c0;
-                __builtin_amdgcn_raw_buffer_store_b32(codes, rs, (row_ok && col < N) ? rowrel * (int)ldc + col
-                                                                                    : 0x7ffffff0, 0, 0);
+                const int off = (int)(((long)(col / kMxBK) * c_cap + rb + rowrel) * kMxBK + col % kMxBK);
+                __builtin_amdgcn_raw_buffer_store_b32(codes, rs, (row_ok && col < N) ? off : 0x7ffffff0, 0, 0);
                 sdw |= (uint32_t)(x + 127) << (8 * jj);
             }
             const bool w_ok = c0 == 0 && row_ok && colw < N;
@@ -87,19 +90,23 @@ __device__ __forceinline__ void store_tile_mx(f32x16 (&acc)[TM][TN], uint8_t* C,
 }
 
 // C[rows of group e, n-tile] = A[rows] @ B_e on MX operands.
-//   A: codes, row r at A + row(r)*lda (row(r) = a_rows[r] when gathering);
-//      scales a_sc + kb*a_sc_kstride + row(r)*4: the 4 bytes of 128-k block kb.
-//   B: expert e's codes at B + e*strideB as 16 KiB tiles [Npad/128][K/128][128 n][128 k];
-//      scales b_sc + e*b_sc_estride + (kb*Npad + n)*4.
-//   EPI 1 / 2: fp32 / 24-bit planes as store_tile32; EPI 3: SiLU, MX codes to
-//   C (ldc bytes per row) and scale dwords to c_sc[N/128][c_cap][4].
-// Requirements (host): K % 128 == 0, K >= 256, N % 128 == 0, lda % 16 == 0.
+//   A: the 64 codes of row r's k-block kb at A + kb*a_kstride + row(r)*a_rstride,
+//      row(r) = a_rows[r] when gathering, else r (row-major: a_kstride = 64,
+//      a_rstride = K; k-blocked [K/64][cap][64]: a_kstride = cap*64,
+//      a_rstride = 64); scales a_sc + ((kb/2)*a_sc_rows + row(r))*4: the 4
+//      bytes of the 128-k pair of blocks.
+//   B: expert e's codes at B + e*strideB as 8 KiB tiles [Npad/128][K/64][128 n][64 k];
+//      scales b_sc + e*b_sc_estride + ((kb/2)*Npad + n)*4.
+//   EPI 1 / 2: fp32 / 24-bit planes as store_tile32 (ldc, c_cap); EPI 3: SiLU,
+//   MX codes to the k-blocked C[N/64][c_cap][64] and scale dwords to c_sc[N/128][c_cap][4].
+// Requirements (host): K % 128 == 0, K >= 128, N % 128 == 0.
 template <int BM, int BN, int NS, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
-    const uint8_t* __restrict__ A, long lda, const int32_t* __restrict__ a_rows, const uint8_t* __restrict__ a_sc,
-    long a_sc_kstride, const uint8_t* __restrict__ B, long strideB, const uint8_t* __restrict__ b_sc,
-    long b_sc_estride, int Npad, void* __restrict__ C, long ldc, long c_cap, uint8_t* __restrict__ c_sc,
-    const int32_t* __restrict__ offsets, int E, int rmin, int rmax, int N, int K, int n_tiles) {
+    const uint8_t* __restrict__ A, long a_kstride, long a_rstride, const int32_t* __restrict__ a_rows,
+    const uint8_t* __restrict__ a_sc, long a_sc_rows, const uint8_t* __restrict__ B,
+    long strideB, const uint8_t* __restrict__ b_sc, long b_sc_estride, int Npad, void* __restrict__ C, long ldc,
+    long c_cap, uint8_t* __restrict__ c_sc, const int32_t* __restrict__ offsets, int E, int rmin, int rmax, int N,
+    int K, int n_tiles) {
     constexpr int NW = WM * WN, BK = kMxBK;
     constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, ASC = BM * 4, BSC = BN * 4;
     constexpr int STAGE = A_BYTES + B_BYTES + ASC + BSC;
@@ -121,10 +128,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
     const uint8_t* a_src[A_CHUNKS];
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-        const int row = (uwave + NW * i) * 8 + l / 8;  // 8 rows of 128 bytes per KiB
-        int grow = min(rb + row, re - 1);             // rows past the group repeat a valid row
+        const int row = (uwave + NW * i) * 16 + l / 4;  // 16 rows of 64 bytes per KiB
+        int grow = min(rb + row, re - 1);              // rows past the group repeat a valid row
         if (a_rows != nullptr) grow = a_rows[grow];
-        a_src[i] = A + (long)grow * lda + 16 * ((l % 8) ^ mx_swz(row));
+        a_src[i] = A + (long)grow * a_rstride + 16 * ((l % 4) ^ mx_swz(row));
     }
     const uint8_t* Be = B + (long)e * strideB;
     const int nb_last = Npad / kMxTileN - 1;
@@ -137,13 +144,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
     }
     // scale dwords: waves 0..BM/64-1 take A rows 64w.., the others B columns
     const uint8_t* s_src;
-    long s_kstep;
+    long s_kstep;  // bytes per 128-k block pair
     uint32_t s_dst;
     if (uwave < BM / 64) {
         int grow = min(rb + 64 * uwave + l, re - 1);
         if (a_rows != nullptr) grow = a_rows[grow];
         s_src = a_sc + (long)grow * 4;
-        s_kstep = a_sc_kstride;
+        s_kstep = a_sc_rows * 4;
         s_dst = A_BYTES + B_BYTES + 256 * uwave;
     } else {
         const int col = min(n0 + 64 * (uwave - BM / 64) + l, Npad - 1);
@@ -156,11 +163,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
         const uint32_t sb = (uint32_t)(uintptr_t)(ring + stage * STAGE);
         const uint32_t b0 = sb + uwave * 1024;
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) lds_dma16(a_src[i] + (long)kb * BK, b0 + i * 1024 * NW);
+        for (int i = 0; i < A_CHUNKS; ++i) lds_dma16(a_src[i] + (long)kb * a_kstride, b0 + i * 1024 * NW);
 #pragma unroll
         for (int i = 0; i < B_CHUNKS; ++i)
             lds_dma16(b_src[i] + (long)kb * kMxTileBytes, b0 + A_BYTES + i * 1024 * NW);
-        lds_dma4(s_src + (long)kb * s_kstep, sb + s_dst);
+        lds_dma4(s_src + (long)(kb >> 1) * s_kstep, sb + s_dst);
     };
 
     f32x16 acc[TM][TN];
@@ -173,47 +180,41 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
 
     const int wm = uwave / WN, wn = uwave % WN, h = l >> 5;
     const bool active = rb + wm * WTM < re;
-    auto compute = [&](lds_u8* St) {
+    auto compute = [&](lds_u8* St, int kb) {
         lds_u8* As = St;
         lds_u8* Bs = St + A_BYTES;
         lds_u8* Asc = St + A_BYTES + B_BYTES;
         lds_u8* Bsc = Asc + ASC;
-        uint32_t sa[TM], sbw[TN];
+        const int sh = 8 * (2 * (kb & 1) + h);  // this lane's 32-k block inside the 128-k scale dword
+        i32x8 af[TM], bfr[TN];
+        uint32_t sa[TM], sbv[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sa[i] = *(lds_u32*)(Asc + (wm * WTM + i * 32 + (l & 31)) * 4);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) sbw[j] = *(lds_u32*)(Bsc + (wn * WTN + j * 32 + (l & 31)) * 4);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {  // two 64-k slices per stage
-            i32x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 32 + (l & 31);
-                lds_u8* base = As + row * BK;
-                const u32x4 lo = *(lds_u32x4*)(base + 16 * ((4 * s + h) ^ mx_swz(row)));
-                const u32x4 hi = *(lds_u32x4*)(base + 16 * ((4 * s + 2 + h) ^ mx_swz(row)));
-                af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
-                              (int)hi[3]};
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = wn * WTN + j * 32 + (l & 31);
-                const int nn = n % kMxTileN;
-                lds_u8* base = Bs + (n / kMxTileN) * kMxTileBytes + nn * BK;
-                const u32x4 lo = *(lds_u32x4*)(base + 16 * ((4 * s + h) ^ mx_swz(nn)));
-                const u32x4 hi = *(lds_u32x4*)(base + 16 * ((4 * s + 2 + h) ^ mx_swz(nn)));
-                bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
-                               (int)hi[3]};
-            }
-            const int sh = 8 * (2 * s + h);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bfr[j], acc[i][j], 0, 0, 0, (int)((sa[i] >> sh) & 0xffu), 0,
-                        (int)((sbw[j] >> sh) & 0xffu));
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (l & 31);
+            lds_u8* base = As + row * BK;
+            const u32x4 lo = *(lds_u32x4*)(base + 16 * (h ^ mx_swz(row)));
+            const u32x4 hi = *(lds_u32x4*)(base + 16 * ((2 + h) ^ mx_swz(row)));
+            af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                          (int)hi[3]};
+            sa[i] = (*(lds_u32*)(Asc + row * 4) >> sh) & 0xffu;
         }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = wn * WTN + j * 32 + (l & 31);
+            const int nn = n % kMxTileN;
+            lds_u8* base = Bs + (n / kMxTileN) * kMxTileBytes + nn * BK;
+            const u32x4 lo = *(lds_u32x4*)(base + 16 * (h ^ mx_swz(nn)));
+            const u32x4 hi = *(lds_u32x4*)(base + 16 * ((2 + h) ^ mx_swz(nn)));
+            bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                           (int)hi[3]};
+            sbv[j] = (*(lds_u32*)(Bsc + n * 4) >> sh) & 0xffu;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0,
+                                                                            (int)sa[i], 0, (int)sbv[j]);
     };
 
     const int nsteps = K / BK;  // >= 2
@@ -227,12 +228,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
         asm volatile("" ::: "memory");
         if (s + NS - 1 < nsteps) issue((s + NS - 1) % NS, s + NS - 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (active) compute(ring + (s % NS) * STAGE);
+        if (active) compute(ring + (s % NS) * STAGE, s);
         __builtin_amdgcn_sched_barrier(0);
     }
     if (!active) return;
     if constexpr (EPI == 3)
-        store_tile_mx<TM, TN, WTM, WTN>(acc, (uint8_t*)C, ldc, c_cap, c_sc, rb, re, n0, N, wm, wn);
+        store_tile_mx<TM, TN, WTM, WTN>(acc, (uint8_t*)C, c_cap, c_sc, rb, re, n0, N, wm, wn);
     else
         store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, wm, wn);
 }

@@ -311,23 +311,24 @@ hipError_t run_fp8_cfg(TileCfg cfg, const void* A, long lda, const int32_t* a_ro
                                    s);
 }
 
-// MX fp8 shape (gemm_mx_kernel): 256 x 256 tiles, 128-k stages of 66 KB
-// (codes of A and B plus their scale dwords), a 2-stage ring, 8 waves.
+// MX fp8 shape (gemm_mx_kernel): 256 x 256 tiles, 64-k stages of 34 KB
+// (codes of A and B plus their scale dwords), a 4-stage ring, 8 waves.
 struct MxLarge {
-    static constexpr int BM = 256, BN = 256, NS = 2, WM = 4, WN = 2;
+    static constexpr int BM = 256, BN = 256, NS = 4, WM = 4, WN = 2;
 };
 
 template <class C, int EPI>
-hipError_t run_mx(const void* A, long lda, const int32_t* a_rows, const void* a_sc, long a_sc_kstride, const void* B,
-                  long strideB, const void* b_sc, long b_sc_estride, int Npad, void* Cm, long ldc, long c_cap,
-                  void* c_sc, const int32_t* offsets, int E, int max_rows, int N, int K, hipStream_t s) {
+hipError_t run_mx(const void* A, long a_kstride, long a_rstride, const int32_t* a_rows, const void* a_sc,
+                  long a_sc_rows, const void* B, long strideB, const void* b_sc, long b_sc_estride, int Npad,
+                  void* Cm, long ldc, long c_cap, void* c_sc, const int32_t* offsets, int E, int max_rows, int N,
+                  int K, hipStream_t s) {
     const int n_tiles = (N + C::BN - 1) / C::BN;
     const long grid = max_mtiles(C::BM, offsets, E, 0, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm_mx_kernel<C::BM, C::BN, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
-                       dim3(C::WM * C::WN * 64), 0, s, (const uint8_t*)A, lda, a_rows, (const uint8_t*)a_sc,
-                       a_sc_kstride, (const uint8_t*)B, strideB, (const uint8_t*)b_sc, b_sc_estride, Npad, Cm, ldc,
-                       c_cap, (uint8_t*)c_sc, offsets, E, 0, INT_MAX, N, K, n_tiles);
+                       dim3(C::WM * C::WN * 64), 0, s, (const uint8_t*)A, a_kstride, a_rstride, a_rows,
+                       (const uint8_t*)a_sc, a_sc_rows, (const uint8_t*)B, strideB, (const uint8_t*)b_sc,
+                       b_sc_estride, Npad, Cm, ldc, c_cap, (uint8_t*)c_sc, offsets, E, 0, INT_MAX, N, K, n_tiles);
     return hipGetLastError();
 }
 
@@ -470,23 +471,26 @@ hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int
     return run_fp8_cfg<kEpiF32Out>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, 0, offsets, E, max_rows, H, F, s);
 }
 
-bool ffn_mx_ok(int H, int F) { return H % 128 == 0 && F % 128 == 0 && H >= 256 && F >= 256; }
+bool ffn_mx_ok(int H, int F) { return H % 128 == 0 && F % 128 == 0 && H >= 128 && F >= 128; }
 
-hipError_t launch_ffn_up_mx(const void* xq, const void* xs, int T, const int32_t* row_token, const int32_t* offsets,
-                            int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H, int F, void* hq,
-                            void* hs, long cap, hipStream_t s) {
-    return run_mx<MxLarge, 3>(xq, H, row_token, xs, (long)T * 4, W1q, mx_weight_bytes(1, H, F), W1s,
-                              mx_weight_scale_bytes(1, H, F), F, hq, F, cap, hs, offsets, E, max_rows, F, H, s);
+hipError_t launch_ffn_up_mx(const void* xq, const void* xs, long x_rows, const int32_t* row_token,
+                            const int32_t* offsets, int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H,
+                            int F, void* hq, void* hs, long cap, hipStream_t s) {
+    // A: row-major token codes xq[x_rows][H] gathered through row_token, scales [H/128][x_rows][4]
+    return run_mx<MxLarge, 3>(xq, dma::kMxBK, H, row_token, xs, x_rows, W1q, mx_weight_bytes(1, H, F), W1s,
+                              mx_weight_scale_bytes(1, H, F), F, hq, 0, cap, hs, offsets, E, max_rows, F, H, s);
 }
 
 hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const int32_t* offsets, int E, int max_rows,
                               const uint8_t* W2q, const uint8_t* W2s, int F, int H, bool packed, void* y,
                               hipStream_t s) {
+    // A: the k-blocked h codes [F/64][cap][64] of the W1 launch, scales [F/128][cap][4]
+    const long ks = cap * dma::kMxBK;
     if (packed)
-        return run_mx<MxLarge, kEpiPacked24>(hq, F, nullptr, hs, cap * 4, W2q, mx_weight_bytes(1, F, H), W2s,
+        return run_mx<MxLarge, kEpiPacked24>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
                                              mx_weight_scale_bytes(1, F, H), H, y, H, cap, nullptr, offsets, E,
                                              max_rows, H, F, s);
-    return run_mx<MxLarge, kEpiF32Out>(hq, F, nullptr, hs, cap * 4, W2q, mx_weight_bytes(1, F, H), W2s,
+    return run_mx<MxLarge, kEpiF32Out>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
                                        mx_weight_scale_bytes(1, F, H), H, y, H, 0, nullptr, offsets, E, max_rows, H,
                                        F, s);
 }

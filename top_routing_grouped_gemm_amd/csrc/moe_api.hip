@@ -509,26 +509,37 @@ int moe_quantize_mxfp8_rows(const void* x, int T, int H, moe_dtype_t dt, uint8_t
                             hipStream_t stream) {
     if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
     if (T < 1 || H < 1) return MOE_ERR_INVALID_ARG;
-    if (H % 128 != 0 || (long long)T * H / 4 >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+    if (H % 128 != 0 || (long long)T * H >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
     if (!x || !xq || !x_scale) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_quantize_mx_rows(x, T, H, (Dtype)dt, xq, x_scale, stream));
+    return hip_status(
+        moe::launch_quantize_mx_rows(x, T, H, (Dtype)dt, xq, x_scale, stream));
 }
 
-int moe_grouped_ffn_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const int32_t* row_token,
-                          const int32_t* expert_offsets, const uint8_t* W1q, const uint8_t* W1_scale,
-                          const uint8_t* W2q, const uint8_t* W2_scale, int T, int H, int F, int E, int k,
-                          uint8_t* h_codes, uint8_t* h_scale, float* y_perm, hipStream_t stream) {
+size_t moe_grouped_ffn_mxfp8_workspace_bytes(int T, int H, int k) {
+    if (T < 1 || H < 1 || k < 1 || k > kMaxK || H % 128 != 0) return 0;
+    return align_up((size_t)T * H) + align_up((size_t)(H / 128) * T * 4);
+}
+
+int moe_grouped_ffn_mxfp8(const void* x, const int32_t* row_token, const int32_t* expert_offsets,
+                          const uint8_t* W1q, const uint8_t* W1_scale, const uint8_t* W2q, const uint8_t* W2_scale,
+                          int T, int H, int F, int E, int k, uint8_t* h_codes, uint8_t* h_scale, float* y_perm,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
     if (F < 1) return MOE_ERR_INVALID_ARG;
     int st = check_sizes(T, H, F, E, k);
     if (st != MOE_OK) return st;
     if (!moe::ffn_mx_ok(H, F)) return MOE_ERR_UNSUPPORTED;
     if ((long long)T * k * F >= (1LL << 31) || (long long)T * k * H * 4 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
-    if (!xq || !x_scale || !row_token || !expert_offsets || !W1q || !W1_scale || !W2q || !W2_scale || !h_codes ||
-        !h_scale || !y_perm)
+    if (!x || !row_token || !expert_offsets || !W1q || !W1_scale || !W2q || !W2_scale || !h_codes || !h_scale ||
+        !y_perm || !ws)
         return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe_grouped_ffn_mxfp8_workspace_bytes(T, H, k)) return MOE_ERR_WORKSPACE;
     const long rows = (long)T * k;
-    MOE_TRY(moe::launch_ffn_up_mx(xq, x_scale, T, row_token, expert_offsets, E, (int)rows, W1q, W1_scale, H, F,
-                                  h_codes, h_scale, rows, stream));
+    uint8_t* xq = (uint8_t*)ws;
+    uint8_t* xs = xq + align_up((size_t)T * H);
+    // quantise the token rows once; the W1 launch gathers their codes through row_token
+    MOE_TRY(moe::launch_quantize_mx_rows(x, T, H, moe::kBF16, xq, xs, stream));
+    MOE_TRY(moe::launch_ffn_up_mx(xq, xs, T, row_token, expert_offsets, E, (int)rows, W1q, W1_scale, H, F, h_codes,
+                                  h_scale, rows, stream));
     return hip_status(moe::launch_ffn_down_mx(h_codes, h_scale, rows, expert_offsets, E, (int)rows, W2q, W2_scale, F,
                                               H, false, y_perm, stream));
 }
@@ -561,7 +572,7 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
     const long rows = (long)T * k;
     uint8_t* xq = (uint8_t*)(base + L.xq);
     uint8_t* xs = (uint8_t*)(base + L.xs);
-    // the router keeps bf16 x; the experts read x quantised to MX before dispatch (gathered by the W1 launch)
+    // the router keeps bf16 x; the experts read x quantised to MX once per token (gathered by the W1 launch)
     MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, moe::kBF16, ids, w, base + L.route, stream));
     if ((st = enqueue_permute(x, ids, w, T, H, E, k, MOE_BF16, nullptr, off, row_token, iv,
                               (int32_t*)(base + L.partial), false, stream)) != MOE_OK)

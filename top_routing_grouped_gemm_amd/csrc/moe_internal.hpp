@@ -95,21 +95,21 @@ hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int
                                const float* s2, int F, int H, TileCfg cfg, bool packed, void* y, long cap,
                                hipStream_t s);
 
-// MX fp8 (mx_quant.hip, gemm_mx.hpp): token rows quantised before dispatch to
-// codes xq[T][H] + scales xs[H/128][T][4]; expert weights [E][K][N] to code
-// tiles (mx_weight_bytes) + scales (mx_weight_scale_bytes). The W1 launch
-// gathers xq rows through row_token and writes SiLU(h) as MX codes hq[cap][F]
-// + scales hs[F/128][cap][4]; the W2 launch writes y as fp32 [cap][H] or the
-// 24-bit planes (packed). Needs H, F multiples of 128 and >= 256.
+// MX fp8 (mx_quant.hip, gemm_mx.hpp). Rows: R rows of x to row-major codes
+// [R][H] and scales [H/128][R][4]. Weights [E][K][N] to code tiles (mx_weight_bytes) + scales
+// (mx_weight_scale_bytes). The W1 launch gathers row-major token codes
+// xq[x_rows][H] through row_token and writes SiLU(h) as k-blocked MX codes hq[F/64][cap][64] + scales
+// hs[F/128][cap][4]; the W2 launch writes y as fp32 [cap][H] or the 24-bit
+// planes (packed). H, F multiples of 128.
 long mx_weight_bytes(int E, int K, int N);
 long mx_weight_scale_bytes(int E, int K, int N);
-hipError_t launch_quantize_mx_rows(const void* x, int T, int H, Dtype dt, uint8_t* xq, uint8_t* xs, hipStream_t s);
+hipError_t launch_quantize_mx_rows(const void* x, long R, int H, Dtype dt, uint8_t* xq, uint8_t* xs, hipStream_t s);
 hipError_t launch_quantize_mx_weights(const void* W, int E, int K, int N, Dtype dt, uint8_t* Wq, uint8_t* Ws,
                                       hipStream_t s);
 bool ffn_mx_ok(int H, int F);
-hipError_t launch_ffn_up_mx(const void* xq, const void* xs, int T, const int32_t* row_token, const int32_t* offsets,
-                            int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H, int F, void* hq,
-                            void* hs, long cap, hipStream_t s);
+hipError_t launch_ffn_up_mx(const void* xq, const void* xs, long x_rows, const int32_t* row_token,
+                            const int32_t* offsets, int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H,
+                            int F, void* hq, void* hs, long cap, hipStream_t s);
 hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const int32_t* offsets, int E, int max_rows,
                               const uint8_t* W2q, const uint8_t* W2s, int F, int H, bool packed, void* y,
                               hipStream_t s);
