@@ -111,8 +111,9 @@ __global__ __launch_bounds__(256) void combine_packed_kernel(const u32x4* __rest
                 const int r = j < k ? inv[t * k + j] : -1;
                 ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
                 const long g = (long)(r >= 0 ? r : 0) * H8 + c;
-                vh[u] = r >= 0 ? hi[g] : u32x4{0u, 0u, 0u, 0u};
-                vl[u] = r >= 0 ? lo[g] : u32x2{0u, 0u};
+                // each y_perm value is read exactly once: non-temporal loads
+                vh[u] = r >= 0 ? __builtin_nontemporal_load(hi + g) : u32x4{0u, 0u, 0u, 0u};
+                vl[u] = r >= 0 ? __builtin_nontemporal_load(lo + g) : u32x2{0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {

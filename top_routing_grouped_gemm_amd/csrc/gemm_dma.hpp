@@ -81,6 +81,14 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
 
+// The same load with the non-temporal cache policy: for weights a launch
+// streams once (the few-row shapes read every expert slab exactly once), so
+// they do not displace reused lines. Measured at decode: grouped FFN 126 ->
+// 112 us (bf16), 71 -> 66 us (fp8 codes).
+__device__ __forceinline__ void lds_dma16_nt(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+
 __device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int swz_b(int row, int chunk) { return chunk ^ (2 * ((row & 3) + 4 * ((row >> 3) & 1))); }
 
@@ -382,7 +390,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
 #pragma unroll
         for (int i = 0; i < Tl::A_CHUNKS; ++i) lds_dma16(a_src[i] + (long)k0 * a_kstep, b0 + i * 1024 * NW);
 #pragma unroll
-        for (int i = 0; i < Tl::B_CHUNKS; ++i) lds_dma16(b_src[i] + (long)k0 * b_kbytes, b0 + A_BYTES + i * 1024 * NW);
+        for (int i = 0; i < Tl::B_CHUNKS; ++i) {
+            // few-row tiles (BM <= 32) stream each weight slab once: non-temporal
+            if constexpr (BM <= 32) lds_dma16_nt(b_src[i] + (long)k0 * b_kbytes, b0 + A_BYTES + i * 1024 * NW);
+            else lds_dma16(b_src[i] + (long)k0 * b_kbytes, b0 + A_BYTES + i * 1024 * NW);
+        }
     };
 
     f32x16 acc[TM][TN];
