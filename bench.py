@@ -100,6 +100,20 @@ def bytes_model(I, A, experts_hit):
     }
 
 
+def library_dense_gemm(M, K, N, reps=20):
+    """Context for the grouped-GEMM roofline: the vendor library's dense bf16 GEMM (torch.mm -> hipBLASLt) with
+    the same FLOPs as one expert launch (all rows in one matrix, no gather, no grouping). Returns ms."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+    c = torch.mm(a, b)
+    t = event_time_ms(lambda: torch.mm(a, b, out=c), reps, torch.cuda.current_stream())
+    del a, b, c
+    return t
+
+
 def run_workload(name, steps, warmup, stage_reps):
     import numpy as np
     import torch
@@ -482,6 +496,12 @@ def main():
         },
         "prefill": pre,
     }
+    up = library_dense_gemm(pre["A"], I.H, I.F)
+    down = library_dense_gemm(pre["A"], I.F, I.H)
+    line["roofline"]["library_dense_gemm"] = {
+        "what": "torch.mm (hipBLASLt) bf16 dense GEMMs of the same FLOPs (A x H x F and A x F x H), no grouping",
+        "ms": round(up + down, 4), "tflops": round(pre["grouped_ffn_flops"] / ((up + down) * 1e-3) / 1e12, 1),
+        "frac": round(pre["grouped_ffn_flops"] / ((up + down) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_decode:
         Id, dec = run_workload("decode", max(args.steps, 50), args.warmup, max(args.stage_reps, 100))
         wbytes = dec["experts_hit"] * 2 * Id.H * Id.F * Id.elem_bytes
