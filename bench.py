@@ -222,7 +222,7 @@ def capacity_times(name, factor, reps=50):
     t_plain = event_time_ms(plain, reps, s)
     t_cap = event_time_ms(capped, reps, s)
     after = int(torch.bincount(ids.flatten().long(), minlength=E).max())
-    cap = int(np.ceil(T * k / E * np.float64(np.float32(factor))))
+    cap = int(np.ceil(T * k / E * float(factor)))
     return {"workload": name, "capacity_factor": factor, "capacity": cap, "route_ms": round(t_plain, 5),
             "route_capacity_ms": round(t_cap, 5), "max_rows_per_expert": {"plain": before, "capped": after}}
 

@@ -124,7 +124,10 @@ int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, in
  * capacity = tokens * k / experts * 1.2 selections; an over-capacity expert's
  * logit is set to -inf for the excess tokens, which choose again.
  *
- *   cap = ceil(T * k / E * cap_factor)   (double precision, in that order)
+ *   cap = ceil(T * k / E * cap_factor)   (double precision, in that order;
+ *                                         cap_factor is a double so that a
+ *                                         factor such as 1.2 enters exactly
+ *                                         as the caller's double holds it)
  *   tokens in ascending id each take the k largest logits among experts
  *   selected fewer than cap times by the tokens before them (ties to the
  *   lower id); weights and drop as in moe_route, over the final selection.
@@ -139,7 +142,7 @@ int moe_route(const void* x, const void* Wr, const float* bias, int T, int H, in
  */
 size_t moe_route_capacity_workspace_bytes(int T, int H, int E, moe_dtype_t dt);
 int moe_route_capacity(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
-                       float drop_thresh, float cap_factor, moe_dtype_t dt, int32_t* topk_ids,
+                       float drop_thresh, double cap_factor, moe_dtype_t dt, int32_t* topk_ids,
                        float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*

@@ -86,7 +86,12 @@ def test_select_capacity_converges_in_rounds(dev):
     _check_select(dev, lg32, k, cap, 0.0)
 
 
-@pytest.mark.parametrize("name,over", [("decode", {}), ("skew", {"seed": 2011})])
+@pytest.mark.parametrize("name,over", [
+    ("decode", {}),
+    ("skew", {"seed": 2011}),
+    # T*k/E*1.2 = 36 exactly: the factor must enter as the double 1.2 (a float 1.2 gave capacity 37)
+    ("tiny", {"T": 400, "H": 384, "F": 256, "E": 40, "k": 3, "zipf": 1.2, "dtype": "bf16", "seed": 3011}),
+])
 def test_route_capacity_from_x(dev, name, over):
     I = gen.make_inputs(name, **over)
     r = oracle.route_capacity(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.k, I.drop, 1.2)

@@ -64,7 +64,7 @@ def load_library(path: Optional[str] = None):
     lib.moe_route.restype = i32
     lib.moe_route_capacity_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.moe_route_capacity_workspace_bytes.restype = sz
-    lib.moe_route_capacity.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+    lib.moe_route_capacity.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, ctypes.c_double, i32, vp, vp, vp, sz, vp]
     lib.moe_route_capacity.restype = i32
     lib.moe_select_capacity_workspace_bytes.argtypes = [i32, i32]
     lib.moe_select_capacity_workspace_bytes.restype = sz

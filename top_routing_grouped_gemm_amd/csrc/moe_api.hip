@@ -308,14 +308,14 @@ int moe_select_capacity(const float* logits, int T, int E, int k, float drop_thr
 }
 
 int moe_route_capacity(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
-                       float drop_thresh, float cap_factor, moe_dtype_t dt, int32_t* topk_ids, float* topk_w,
+                       float drop_thresh, double cap_factor, moe_dtype_t dt, int32_t* topk_ids, float* topk_w,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
     int st = check_sizes(T, H, 0, E, k);
     if (st != MOE_OK) return st;
     if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
-    if (!(cap_factor > 0.0f) || !(cap_factor <= 1e6f)) return MOE_ERR_INVALID_ARG;  // rejects NaN and inf
-    const double capd = ceil((double)T * k / E * (double)cap_factor);
+    if (!(cap_factor > 0.0) || !(cap_factor <= 1e6)) return MOE_ERR_INVALID_ARG;  // rejects NaN and inf
+    const double capd = ceil((double)T * k / E * cap_factor);
     const int cap = capd >= 2147483647.0 ? 2147483647 : (int)capd;
     if ((st = capacity_args(T, E, k, cap)) != MOE_OK) return st;
     if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
