@@ -1,6 +1,6 @@
 """Seeded random-shape GPU parity sweep.
 
-Twenty layers with shapes drawn from a fixed seed (tokens, widths, expert
+Forty layers with shapes drawn from a fixed seed (tokens, widths, expert
 counts, top-k, drop threshold, skewed router bias, shared expert, fp32 or
 bf16) run through every entry point the shape admits, each against the
 oracle:
@@ -37,7 +37,7 @@ def _draw_configs(n=20, seed=2024):
         F = int(rng.choice([64, 128, 256, 384, 512, 8 * int(rng.integers(1, 60))]))
         E = int(rng.choice([1, 2, 4, 8, 16, 24, 40, 64, 128, 300]))
         k = int(rng.integers(1, min(E, 8) + 1))
-        T = int(rng.choice([1, 3, 17, 64, 100, 257, 400]))
+        T = int(rng.choice([1, 3, 17, 64, 100, 257, 400, 1000, 2000]))
         drop = float(rng.choice([0.0, 0.0, 0.05, 0.1])) if k > 1 else 0.0
         drop = min(drop, 1.0 / k)
         zipf = float(rng.choice([0.0, 1.2])) if E >= 4 else 0.0
@@ -46,7 +46,7 @@ def _draw_configs(n=20, seed=2024):
     return out
 
 
-CONFIGS = _draw_configs()
+CONFIGS = _draw_configs(40)
 
 
 def _check_y(y_gpu, y_ref, tol=Y_TOL):
