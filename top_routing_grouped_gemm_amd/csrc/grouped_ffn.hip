@@ -9,7 +9,7 @@
 // prefill many.
 //
 //   up:   h[r]      = silu(x_perm[r] @ W1[e])   (SiLU fused in the epilogue)
-//   down: y_perm[r] = h[r] @ W2[e]              (fp32 out)
+//   down: y_perm[r] = h[r] @ W2[e]              (fp32 out, or 24-bit planes)
 //
 // Scheduling: the M-tiles of all experts form one ragged sequence (expert e
 // contributes ceil(count_e / BM) tiles); each workgroup takes one (M-tile,
@@ -18,10 +18,14 @@
 // sized for the worst case (ceil(rows/BM) + min(E, rows) M-tiles) and
 // workgroups past the last tile exit at once.
 //
-// Large row counts (>= 96 rows per expert on average) run the direct-to-LDS
-// pipeline of gemm_dma.hpp; smaller ones run the register-staged kernel below:
-// 256 threads (4 waves), BM x BN x 64 tiles staged in LDS with one prefetched
-// stage in flight, 16x16x32 bf16 MFMA, fp32 accumulation.
+// bf16 shapes the direct-to-LDS pipeline of gemm_dma.hpp takes (K a multiple
+// of its k-stage, 16-byte rows) run there, in a shape chosen from the mean
+// rows per expert (choose_tile): 256x256 tiles for >= 96, 32-row weight-
+// streaming tiles for < 24, both over disjoint groups in between. Other bf16
+// shapes run the register-staged kernel below (256 threads, BM x BN x 64 tiles
+// staged in LDS with one prefetched stage in flight, 16x16x32 bf16 MFMA, fp32
+// accumulation); fp32 inputs run the plain-FMA kernel. The fp8-weight (F8B)
+// and MX fp8 variants use the same schedule on the shapes further down.
 #include <math.h>
 
 #include <limits.h>
@@ -246,7 +250,8 @@ hipError_t run_bf16(const void* A, long lda, const void* B, long strideB, long l
 //    ring (80 KB) let two workgroups share a CU, so ~120 KB of weight loads
 //    stay in flight per CU and one workgroup's pipeline fill overlaps the
 //    other's tail (measured: 6 stages with one workgroup per CU streamed
-//    4.7 TB/s, 4 stages with two 5.5 TB/s).
+//    4.7 TB/s, 4 stages with two 5.5 TB/s; with non-temporal weight loads
+//    6.1-6.2 TB/s).
 template <int BM_, int BN_, int BK_, int NS_, int WM_, int WN_>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
