@@ -83,6 +83,8 @@ def test_route_rejects(lib):
     assert call(dt=3) == moe.MOE_ERR_INVALID_ARG
     assert call(H=12) == moe.MOE_ERR_UNSUPPORTED
     assert call(E=2000, k=2) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=1025, k=2) == moe.MOE_ERR_UNSUPPORTED   # one past the expert limit
+    assert call(T=4, E=64, k=33) == moe.MOE_ERR_UNSUPPORTED  # one past the top-k limit
     # a split router (few tokens, long H) needs its partial-logit workspace
     need = lib.moe_route_workspace_bytes(32, 2048, 128, 1)
     assert need == 32 * 32 * 128 * 4

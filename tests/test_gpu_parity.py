@@ -122,6 +122,9 @@ SMALL = [
     ("tiny", {"T": 64, "H": 64, "F": 128, "E": 4, "k": 2, "dtype": "bf16", "seed": 84, "Fs": 64}),  # shared
     ("tiny", {"T": 90, "H": 72, "F": 40, "E": 12, "k": 2, "dtype": "f32", "seed": 85, "Fs": 24, "drop": 0.2}),
     ("tiny", {"T": 520, "H": 64, "F": 64, "E": 300, "k": 6, "dtype": "bf16", "seed": 86}),  # E > 256, E%8 != 0 rows
+    # the size limits: E = 1024 experts, top-32
+    ("tiny", {"T": 40, "H": 64, "F": 64, "E": 1024, "k": 32, "dtype": "bf16", "seed": 96}),
+    ("tiny", {"T": 24, "H": 64, "F": 40, "E": 1024, "k": 32, "dtype": "f32", "seed": 97, "drop": 0.02}),
     # large-tile (direct-to-LDS) path: K % 64 == 0, >= 96 rows per expert, partial N tiles
     ("tiny", {"T": 700, "H": 128, "F": 192, "E": 5, "k": 2, "dtype": "bf16", "seed": 87}),
     ("tiny", {"T": 300, "H": 256, "F": 320, "E": 4, "k": 2, "dtype": "bf16", "seed": 88, "Fs": 192}),
