@@ -51,8 +51,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
                 const int r = j < k ? inv[t * k + j] : -1;
                 ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
                 const long row = (long)(r >= 0 ? r : 0) * H4;
-                v0[u] = r >= 0 ? y_perm[row + c0] : make_float4(0.f, 0.f, 0.f, 0.f);
-                v1[u] = (r >= 0 && two) ? y_perm[row + c1] : make_float4(0.f, 0.f, 0.f, 0.f);
+                // each y_perm value is read exactly once: non-temporal loads
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 q0 = r >= 0 ? __builtin_nontemporal_load((const f32x4*)(y_perm + row + c0)) : z4;
+                const f32x4 q1 = (r >= 0 && two) ? __builtin_nontemporal_load((const f32x4*)(y_perm + row + c1)) : z4;
+                v0[u] = make_float4(q0[0], q0[1], q0[2], q0[3]);
+                v1[u] = make_float4(q1[0], q1[1], q1[2], q1[3]);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {

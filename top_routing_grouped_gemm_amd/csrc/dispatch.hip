@@ -16,8 +16,8 @@
 //   index  - each workgroup ranks its chunk's assignments within their expert
 //            (wave ballots match equal expert ids, LDS combines the 4 waves)
 //            and writes row_token and inv;
-//   copy   - many workgroups stream the token rows into x_perm with 16-byte
-//            loads and stores (HBM-bound: T*H*b read, A*H*b written).
+//   copy   - token-major: each token row is read once and written to its k
+//            destination rows (HBM-bound: T*H*b read, A*H*b written).
 #include "moe_common.hpp"
 #include "moe_internal.hpp"
 
@@ -130,15 +130,14 @@ __global__ __launch_bounds__(kDispatchChunk) void index_kernel(const int32_t* __
     __syncthreads();
     if (kept && rank == 0) wc[wv][e] = cnt;
     __syncthreads();
+    int r = -1;
     if (valid) {
         if (kept) {
-            int r = partial[(long)blockIdx.x * E + e] + rank;
+            r = partial[(long)blockIdx.x * E + e] + rank;
             for (int i = 0; i < wv; ++i) r += wc[i][e];
             row_token[r] = a / k;
-            inv[a] = r;
-        } else {
-            inv[a] = -1;
         }
+        inv[a] = r;
     }
 }
 
@@ -212,37 +211,38 @@ __global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int3
     }
 }
 
-// Each wave copies RPW consecutive destination rows: the source token of each
-// row is read once (wave-uniform), then every 16-byte load of all RPW rows is
-// issued before the stores.
-template <int RPW, int VPL>
-__global__ __launch_bounds__(256) void copy_rows_kernel(const u32x4* __restrict__ x,
-                                                        const int32_t* __restrict__ row_token,
-                                                        const int32_t* __restrict__ offsets, int E, int V,
-                                                        u32x4* __restrict__ out) {
-    const int A = offsets[E];
+// Token-major row copy: each wave takes TPW tokens, reads each token row of
+// x once (all TPW rows' loads in flight before any store) and writes it to
+// the k destination rows its assignments got (inv; dropped slots: none), so x
+// is read T*H*b bytes once instead of once per assignment.
+template <int TPW, int VPL>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4* __restrict__ x, const int32_t* __restrict__ inv,
+                                                           int T, int k, int V, u32x4* __restrict__ out) {
     const int wave = threadIdx.x / kWave, l = lane_id();
-    const long r0 = ((long)blockIdx.x * 4 + wave) * RPW;
-    if (r0 >= A) return;
-    long src[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) src[i] = (r0 + i < A) ? (long)row_token[r0 + i] * V : -1;
+    const long t0 = ((long)blockIdx.x * 4 + wave) * TPW;
+    if (t0 >= T) return;
     for (int c0 = 0; c0 < V; c0 += kWave * VPL) {
-        u32x4 v[RPW][VPL];
+        u32x4 v[TPW][VPL];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i)
-#pragma unroll
-            for (int u = 0; u < VPL; ++u) {
-                const int c = c0 + u * kWave + l;
-                if (src[i] >= 0 && c < V) v[i][u] = x[src[i] + c];
-            }
-#pragma unroll
-        for (int i = 0; i < RPW; ++i)
+        for (int i = 0; i < TPW; ++i)
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
                 const int c = c0 + u * kWave + l;
-                if (src[i] >= 0 && c < V) out[(r0 + i) * V + c] = v[i][u];
+                if (t0 + i < T && c < V) v[i][u] = x[(t0 + i) * V + c];
             }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            if (t0 + i >= T) break;
+            for (int j = 0; j < k; ++j) {
+                const int r = inv[(t0 + i) * k + j];  // wave-uniform
+                if (r < 0) continue;
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) {
+                    const int c = c0 + u * kWave + l;
+                    if (c < V) out[(long)r * V + c] = v[i][u];
+                }
+            }
+        }
     }
 }
 
@@ -278,15 +278,17 @@ hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* parti
     return hipGetLastError();
 }
 
-hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                            int row_bytes, void* x_perm, hipStream_t s) {
+hipError_t launch_copy_rows(const void* x, const int32_t* inv, int T, int k, int row_bytes, void* x_perm,
+                            hipStream_t s) {
     const int V = row_bytes / 16;
-    constexpr int RPW = 4, VPL = 4;  // 16 loads of 16 bytes in flight per lane
-    const long rows_per_block = 4L * RPW;
-    const long grid = (max_rows + rows_per_block - 1) / rows_per_block;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((copy_rows_kernel<RPW, VPL>), dim3((unsigned)grid), dim3(256), 0, s, (const u32x4*)x, row_token,
-                       offsets, E, V, (u32x4*)x_perm);
+    if (T == 0) return hipSuccess;
+    if (T >= 4096) {  // 16 loads of 16 bytes in flight per lane
+        hipLaunchKernelGGL((scatter_rows_kernel<4, 4>), dim3((unsigned)((T + 15) / 16)), dim3(256), 0, s,
+                           (const u32x4*)x, inv, T, k, V, (u32x4*)x_perm);
+    } else {  // few tokens: one per wave, for more workgroups
+        hipLaunchKernelGGL((scatter_rows_kernel<1, 4>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
+                           (const u32x4*)x, inv, T, k, V, (u32x4*)x_perm);
+    }
     return hipGetLastError();
 }
 

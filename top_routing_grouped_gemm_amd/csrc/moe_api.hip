@@ -140,7 +140,7 @@ int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, in
         MOE_TRY(moe::launch_scan(partial, moe::dispatch_blocks(n), E, offsets, s));
         MOE_TRY(moe::launch_index(ids, w, partial, n, k, E, row_token, inv, s));
     }
-    if (copy_rows) MOE_TRY(moe::launch_copy_rows(x, row_token, offsets, E, n, (int)(H * elem_bytes(dt)), x_perm, s));
+    if (copy_rows) MOE_TRY(moe::launch_copy_rows(x, inv, T, k, (int)(H * elem_bytes(dt)), x_perm, s));
     return MOE_OK;
 }
 

@@ -52,8 +52,9 @@ hipError_t launch_dispatch_small(const int32_t* ids, const float* w, int n_assig
                                  int32_t* row_token, int32_t* inv, hipStream_t s);
 hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* partial, int n_assign, int k,
                         int E, int32_t* row_token, int32_t* inv, hipStream_t s);
-hipError_t launch_copy_rows(const void* x, const int32_t* row_token, const int32_t* offsets, int E,
-                            int max_rows, int row_bytes, void* x_perm, hipStream_t s);
+// x_perm[inv[t*k+j]] = x[t] for every kept slot (inv >= 0); row_bytes % 16 == 0.
+hipError_t launch_copy_rows(const void* x, const int32_t* inv, int T, int k, int row_bytes, void* x_perm,
+                            hipStream_t s);
 
 // Grouped FFN. Rows of group e are [offsets[e], offsets[e+1]); with offsets == NULL there
 // is a single group of rows [0, fixed_rows) (the shared expert).
