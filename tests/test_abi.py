@@ -90,7 +90,7 @@ def test_route_rejects(lib):
     assert need == 32 * 32 * 128 * 4
     assert call(T=32, H=2048, E=128, k=8) == moe.MOE_ERR_WORKSPACE
     assert call(T=32, H=2048, E=128, k=8, ws=_p(), wsb=need - 1) == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_route_workspace_bytes(8192, 2048, 128, 1) == 4 * 8192 * 128 * 4   # 256 token blocks x 4 splits
+    assert lib.moe_route_workspace_bytes(8192, 2048, 128, 1) == 2 * 8192 * 128 * 4   # 256 token blocks x 2 splits
     assert lib.moe_route_workspace_bytes(65536, 2048, 128, 1) == 0   # enough token blocks: no split
     assert lib.moe_route_workspace_bytes(32, 2048, 128, 0) == 0     # fp32 router never splits
 
