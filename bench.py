@@ -114,7 +114,7 @@ def library_dense_gemm(M, K, N, reps=20):
     return t
 
 
-def run_workload(name, steps, warmup, stage_reps):
+def run_workload(name, steps, warmup, stage_reps, graph=False):
     import numpy as np
     import torch
 
@@ -142,6 +142,25 @@ def run_workload(name, steps, warmup, stage_reps):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t) * 1e3 / steps
+    graph_ms = None
+    if graph:  # the same layer captured once in a HIP graph and replayed (no per-kernel launch from the host)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t) * 1e3 / steps
+        del g
     st, A, counts = stage_times(d, I, stage_reps)
     hit = int((counts > 0).sum())
     flops = 4.0 * A * I.H * I.F + 4.0 * I.T * I.H * I.Fs  # routed experts + shared expert
@@ -151,6 +170,7 @@ def run_workload(name, steps, warmup, stage_reps):
         "rows_per_expert": {"min": int(counts.min()), "max": int(counts.max()),
                             "mean": float(counts.float().mean())},
         "ms_per_step": ms, "tokens_per_s": I.T / (ms * 1e-3),
+        **({"graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": I.T / (graph_ms * 1e-3)}} if graph_ms else {}),
         "stages_ms": {k: round(v, 5) for k, v in st.items()},
         "stage_gbs": {k: round(byts[k] / (st[k] * 1e-3) / 1e9, 1) for k in st},
         "stage_hbm_frac": {k: round(byts[k] / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k in st},
@@ -503,7 +523,7 @@ def main():
         "ms": round(up + down, 4), "tflops": round(pre["grouped_ffn_flops"] / ((up + down) * 1e-3) / 1e12, 1),
         "frac": round(pre["grouped_ffn_flops"] / ((up + down) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_decode:
-        Id, dec = run_workload("decode", max(args.steps, 50), args.warmup, max(args.stage_reps, 100))
+        Id, dec = run_workload("decode", max(args.steps, 50), args.warmup, max(args.stage_reps, 100), graph=True)
         wbytes = dec["experts_hit"] * 2 * Id.H * Id.F * Id.elem_bytes
         dec["weight_stream_gbs"] = round(wbytes / (dec["stages_ms"]["grouped_ffn"] * 1e-3) / 1e9, 1)
         dec["weight_stream_hbm_frac"] = round(dec["weight_stream_gbs"] / PEAK_HBM_GBS, 4)
