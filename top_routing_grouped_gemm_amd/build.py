@@ -47,5 +47,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "forward.c")
+C_EXAMPLE_BIN = os.path.join(ROOT, "tests", "c_abi", "forward")
+
+
+def c_example_cmd(src: str, out: str) -> list:
+    """gcc line of the plain-C caller of the ABI (tests/c_abi/forward.c), linked to libmoe.so by a relative rpath."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rel = os.path.relpath(HERE, os.path.dirname(out))
+    return ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+            f"-I{rocm}/include", src, f"-L{HERE}", "-lmoe", f"-L{rocm}/lib", "-lamdhip64",
+            f"-Wl,-rpath,$ORIGIN/{rel}", f"-Wl,-rpath,{rocm}/lib", "-o", out]
+
+
+def build_c_example(out: str = C_EXAMPLE_BIN) -> str:
+    res = subprocess.run(c_example_cmd(C_EXAMPLE, out), capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_example())
