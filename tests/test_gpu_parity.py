@@ -303,3 +303,39 @@ def test_full_workload(dev, name, nsample):
                                           I.f64(I.W1s()), I.f64(I.W2s()))
     rel = check_y(y[torch.from_numpy(toks).to(dev)].double().cpu().numpy(), yref)
     _say(f"{name}: routing bit-exact over {I.T} tokens; y max-abs/rms {rel:.3e} on {len(toks)} tokens")
+
+
+# ------------------------------------------------ no kept assignments --
+def test_nothing_kept(dev):
+    """A batch whose every slot is dropped (weight 0) or names no expert: permute keeps no row (all offsets 0,
+    inv all -1, row_token and x_perm untouched), the grouped FFN over zero rows writes nothing, and the combine
+    gives 0 (or exactly the shared expert's row)."""
+    T, H, F, E, k = 12, 64, 64, 4, 3
+    x = torch.randn((T, H), device=dev).to(torch.bfloat16)
+    ids = torch.tensor([[0, 1, 2], [5, -1, 4]] * (T // 2), dtype=torch.int32, device=dev)  # even: dropped; odd: no such expert
+    w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    w[1::2] = 0.5                                   # odd tokens: nonzero weights, but every id is out of range
+    sentinel = torch.full((T * k, H), 7.0, device=dev).to(torch.bfloat16)
+    x_perm = sentinel.clone()
+    off = torch.full((E + 1,), 99, dtype=torch.int32, device=dev)
+    row_token = torch.full((T * k,), -5, dtype=torch.int32, device=dev)
+    inv = torch.full((T, k), 99, dtype=torch.int32, device=dev)
+    moe.moe_permute(x, ids, w, E, x_perm=x_perm, expert_offsets=off, row_token=row_token, inv=inv)
+    torch.cuda.synchronize()
+    assert torch.equal(off, torch.zeros_like(off))
+    assert torch.equal(inv, torch.full_like(inv, -1))
+    assert torch.equal(row_token, torch.full_like(row_token, -5)) and torch.equal(x_perm, sentinel)
+
+    W1 = (torch.randn((E, H, F), device=dev) / 8).to(torch.bfloat16)
+    W2 = (torch.randn((E, F, H), device=dev) / 8).to(torch.bfloat16)
+    y_perm = torch.full((T * k, H), 3.0, device=dev)
+    moe.moe_grouped_ffn(x_perm, off, W1, W2, T, k, y_perm=y_perm)
+    torch.cuda.synchronize()
+    assert torch.equal(y_perm, torch.full_like(y_perm, 3.0))
+
+    y = moe.moe_combine(y_perm, inv, w)
+    y_sh = torch.randn((T, H), device=dev)
+    y2 = moe.moe_combine(y_perm, inv, w, y_shared=y_sh)
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.zeros_like(y))
+    assert torch.equal(y2, y_sh)
