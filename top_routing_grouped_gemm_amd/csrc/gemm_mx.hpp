@@ -238,5 +238,156 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
         store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, wm, wn);
 }
 
+// EPI 3 for waves of 32 columns: SiLU, one 32-value block per row and wave,
+// its codes as one dword and its scale as one byte of the row's 128-column
+// scale dword (waves of a workgroup own distinct bytes of it).
+template <int TM>
+__device__ __forceinline__ void store_tile_mx32(f32x16 (&acc)[TM][1], uint8_t* C, long c_cap, uint8_t* c_sc, int rb,
+                                                int re, int colw, int N, int wm, int wtm) {
+    const int l = lane_id();
+    const int c0 = (l & 31) & ~3, m = l & 3;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)((long)(N / kMxBK) * c_cap * kMxBK), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsc =
+        __builtin_amdgcn_make_buffer_rsrc(c_sc, (short)0, (int)((long)(N / kMxTileN) * c_cap * 4), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int rowrel = wm * wtm + i * 32 + 8 * p + 4 * (l >> 5) + m;
+            const bool ok = rowrel < re - rb && colw < N;
+            float v[4] = {acc[i][0][4 * p], acc[i][0][4 * p + 1], acc[i][0][4 * p + 2], acc[i][0][4 * p + 3]};
+            quad_transpose(v);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = silu_f32(v[q]);
+            float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            am = fmaxf(am, __shfl_xor(am, 4));  // the 8 quads of this row's 32-column block
+            am = fmaxf(am, __shfl_xor(am, 8));
+            am = fmaxf(am, __shfl_xor(am, 16));
+            const int x = mx_exponent(am);
+            const uint32_t codes = mx_codes4(v[0], v[1], v[2], v[3], x);
+            const int col = colw + c0;
+            const int off = (int)(((long)(col / kMxBK) * c_cap + rb + rowrel) * kMxBK + col % kMxBK);
+            __builtin_amdgcn_raw_buffer_store_b32(codes, rs, ok ? off : 0x7ffffff0, 0, 0);
+            const int soff = (int)((((long)colw / kMxTileN) * c_cap + rb + rowrel) * 4 + (colw % kMxTileN) / 32);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(x + 127), rsc, (ok && c0 == 0) ? soff : 0x7ffffff0, 0, 0);
+        }
+}
+
+// Weight-streaming MX shape for few rows per group (decode): one 32-row MFMA
+// block against a 128-column weight slab, 4 waves of 32 columns, 128-k stages
+// (two 64-k MX products per stage: A pieces of 128 bytes, B two adjacent 8 KiB
+// code tiles, read non-temporally since each slab is read once), NS-stage
+// ring. Operand and scale layouts, requirements and epilogues as
+// gemm_mx_kernel; per stage each wave issues one A chunk, four B chunks and
+// one 4-byte scale load (wave 0: the 32 rows' A scales; waves 1, 2: B
+// columns 0-63, 64-127; wave 3 repeats wave 2's into a spare slot).
+template <int NS, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_mx_stream_kernel(
+    const uint8_t* __restrict__ A, long a_kstride, long a_rstride, const int32_t* __restrict__ a_rows,
+    const uint8_t* __restrict__ a_sc, long a_sc_rows, const uint8_t* __restrict__ B, long strideB,
+    const uint8_t* __restrict__ b_sc, long b_sc_estride, int Npad, void* __restrict__ C, long ldc, long c_cap,
+    uint8_t* __restrict__ c_sc, const int32_t* __restrict__ offsets, int E, int rmin, int rmax, int N, int K,
+    int n_tiles) {
+    constexpr int BM = 32, BN = kMxTileN, BK2 = 2 * kMxBK, NW = 4;
+    constexpr int A_BYTES = BM * BK2, B_BYTES = BN * BK2, SC = 256;  // scale slots: A, B 0-63, B 64-127, spare
+    constexpr int STAGE = A_BYTES + B_BYTES + 4 * SC;
+    constexpr int LOADS = 1 + 4 + 1;
+    static_assert(A_BYTES == 1024 * NW && B_BYTES == 4 * 1024 * NW, "one A and four B KiB chunks per wave");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+    __shared__ __align__(1024) uint8_t smem[NS * STAGE];
+
+    int e, rb, re, nt;
+    if (!xcd_tile<BM>(offsets, E, 0, n_tiles, rmin, rmax, e, rb, re, nt)) return;
+    const int n0 = nt * BN;
+    const int wave = threadIdx.x / kWave, l = lane_id();
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int KB = K / kMxBK;
+
+    // A chunk of this wave: rows 8*uwave + l/8, 16-byte piece l%8 of the 128-k slice (pieces 0-3 from the
+    // first 64-k block, 4-7 from the second), placed at piece position (l%8) ^ swz(row) of a 128-byte row
+    const int arow = 8 * uwave + l / 8;
+    int grow = min(rb + arow, re - 1);  // rows past the group repeat a valid row
+    if (a_rows != nullptr) grow = a_rows[grow];
+    const int apiece = (l % 8) ^ ((arow >> 1) & 7);
+    const uint8_t* a_src = A + (long)(apiece / 4) * a_kstride + (long)grow * a_rstride + 16 * (apiece % 4);
+    // B chunks: the stage's two tiles are 16 KiB contiguous; chunk c = uwave + 4i
+    const uint8_t* Be = B + (long)e * strideB;
+    const int nb = min(n0 / kMxTileN, Npad / kMxTileN - 1);
+    const uint8_t* b_src = Be + (long)nb * KB * kMxTileBytes + uwave * 1024 + 16 * l;
+    // scale dwords
+    const uint8_t* s_src;
+    long s_kstep;
+    if (uwave == 0) {
+        int srow = min(rb + (l & 31), re - 1);
+        if (a_rows != nullptr) srow = a_rows[srow];
+        s_src = a_sc + (long)srow * 4;
+        s_kstep = a_sc_rows * 4;
+    } else {
+        const int col = min(n0 + 64 * min(uwave - 1, 1) + l, Npad - 1);
+        s_src = b_sc + (long)e * b_sc_estride + (long)col * 4;
+        s_kstep = (long)Npad * 4;
+    }
+    lds_u8* ring = (lds_u8*)smem;
+    auto issue = [&](int stage, int kp) {  // kp: 128-k step
+        const uint32_t sb = (uint32_t)(uintptr_t)(ring + stage * STAGE);
+        lds_dma16(a_src + (long)(2 * kp) * a_kstride, sb + uwave * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lds_dma16_nt(b_src + (long)(2 * kp) * kMxTileBytes + i * 4096, sb + A_BYTES + (uwave + 4 * i) * 1024);
+        lds_dma4(s_src + (long)kp * s_kstep, sb + A_BYTES + B_BYTES + SC * uwave);
+    };
+
+    f32x16 acc[1][1];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[0][0][q] = 0.f;
+    const int h = l >> 5;
+    auto compute = [&](lds_u8* St) {
+        lds_u8* As = St;
+        lds_u8* Bs = St + A_BYTES;
+        lds_u8* Asc = St + A_BYTES + B_BYTES;
+        lds_u8* Bsc = Asc + SC;  // columns 0-127 in the two B slots
+        const int row = l & 31, n = uwave * 32 + (l & 31);
+        const uint32_t sa_dw = *(lds_u32*)(Asc + row * 4);
+        const uint32_t sb_dw = *(lds_u32*)(Bsc + n * 4);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            lds_u8* abase = As + row * BK2;
+            const u32x4 alo = *(lds_u32x4*)(abase + 16 * ((4 * kk + h) ^ ((row >> 1) & 7)));
+            const u32x4 ahi = *(lds_u32x4*)(abase + 16 * ((4 * kk + 2 + h) ^ ((row >> 1) & 7)));
+            lds_u8* bbase = Bs + kk * kMxTileBytes + n * kMxBK;
+            const u32x4 blo = *(lds_u32x4*)(bbase + 16 * (h ^ mx_swz(n)));
+            const u32x4 bhi = *(lds_u32x4*)(bbase + 16 * ((2 + h) ^ mx_swz(n)));
+            const i32x8 af = {(int)alo[0], (int)alo[1], (int)alo[2], (int)alo[3],
+                              (int)ahi[0], (int)ahi[1], (int)ahi[2], (int)ahi[3]};
+            const i32x8 bf = {(int)blo[0], (int)blo[1], (int)blo[2], (int)blo[3],
+                              (int)bhi[0], (int)bhi[1], (int)bhi[2], (int)bhi[3]};
+            const int sh = 8 * (2 * kk + h);
+            acc[0][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[0][0], 0, 0, 0,
+                                                                        (int)((sa_dw >> sh) & 0xffu), 0,
+                                                                        (int)((sb_dw >> sh) & 0xffu));
+        }
+    };
+
+    const int nsteps = K / BK2;  // >= 1
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nsteps) issue(s, s);
+    for (int s = 0; s < nsteps; ++s) {
+        wait_stage<LOADS, NS - 2>(min(NS - 2, nsteps - 1 - s));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + NS - 1 < nsteps) issue((s + NS - 1) % NS, s + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ring + (s % NS) * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (EPI == 3)
+        store_tile_mx32<1>(acc, (uint8_t*)C, c_cap, c_sc, rb, re, n0 + 32 * uwave, N, 0, BM);
+    else
+        store_tile32<1, 1, BM, 32, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, 0, uwave);
+}
+
 }  // namespace dma
 }  // namespace moe

@@ -322,19 +322,58 @@ struct MxLarge {
     static constexpr int BM = 256, BN = 256, NS = 4, WM = 4, WN = 2;
 };
 
+// Weight-streaming MX shape (dma::gemm_mx_stream_kernel): 32 x 128 tiles,
+// 128-k stages of 21 KB in a 3-stage ring, two workgroups per CU.
+constexpr int kMxStreamNS = 3;
+
 template <class C, int EPI>
 hipError_t run_mx(const void* A, long a_kstride, long a_rstride, const int32_t* a_rows, const void* a_sc,
                   long a_sc_rows, const void* B, long strideB, const void* b_sc, long b_sc_estride, int Npad,
                   void* Cm, long ldc, long c_cap, void* c_sc, const int32_t* offsets, int E, int max_rows, int N,
-                  int K, hipStream_t s) {
+                  int K, hipStream_t s, int rmin = 0, int rmax = INT_MAX) {
     const int n_tiles = (N + C::BN - 1) / C::BN;
     const long grid = max_mtiles(C::BM, offsets, E, 0, max_rows) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm_mx_kernel<C::BM, C::BN, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
                        dim3(C::WM * C::WN * 64), 0, s, (const uint8_t*)A, a_kstride, a_rstride, a_rows,
                        (const uint8_t*)a_sc, a_sc_rows, (const uint8_t*)B, strideB, (const uint8_t*)b_sc,
-                       b_sc_estride, Npad, Cm, ldc, c_cap, (uint8_t*)c_sc, offsets, E, 0, INT_MAX, N, K, n_tiles);
+                       b_sc_estride, Npad, Cm, ldc, c_cap, (uint8_t*)c_sc, offsets, E, rmin, rmax, N, K, n_tiles);
     return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t run_mx_stream(const void* A, long a_kstride, long a_rstride, const int32_t* a_rows, const void* a_sc,
+                         long a_sc_rows, const void* B, long strideB, const void* b_sc, long b_sc_estride, int Npad,
+                         void* Cm, long ldc, long c_cap, void* c_sc, const int32_t* offsets, int E, int max_rows,
+                         int N, int K, hipStream_t s, int rmin = 0, int rmax = INT_MAX) {
+    const int n_tiles = (N + dma::kMxTileN - 1) / dma::kMxTileN;
+    const long grid = max_mtiles(32, offsets, E, 0, max_rows) * n_tiles + dma::kXcds;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dma::gemm_mx_stream_kernel<kMxStreamNS, EPI>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const uint8_t*)A, a_kstride, a_rstride, a_rows, (const uint8_t*)a_sc, a_sc_rows,
+                       (const uint8_t*)B, strideB, (const uint8_t*)b_sc, b_sc_estride, Npad, Cm, ldc, c_cap,
+                       (uint8_t*)c_sc, offsets, E, rmin, rmax, N, K, n_tiles);
+    return hipGetLastError();
+}
+
+// The MX products over all groups in the regimes of choose_tile: 256-row
+// tiles, 32-row weight-streaming tiles, or both over disjoint groups.
+template <int EPI>
+hipError_t run_mx_cfg(const void* A, long a_kstride, long a_rstride, const int32_t* a_rows, const void* a_sc,
+                      long a_sc_rows, const void* B, long strideB, const void* b_sc, long b_sc_estride, int Npad,
+                      void* Cm, long ldc, long c_cap, void* c_sc, const int32_t* offsets, int E, int max_rows, int N,
+                      int K, hipStream_t s) {
+    const TileCfg cfg = choose_tile(max_rows, E);
+    if (cfg == kTileM128)
+        return run_mx<MxLarge, EPI>(A, a_kstride, a_rstride, a_rows, a_sc, a_sc_rows, B, strideB, b_sc, b_sc_estride,
+                                    Npad, Cm, ldc, c_cap, c_sc, offsets, E, max_rows, N, K, s);
+    const int split = cfg == kTileMixed ? kStreamRows : INT_MAX;
+    const hipError_t e = run_mx_stream<EPI>(A, a_kstride, a_rstride, a_rows, a_sc, a_sc_rows, B, strideB, b_sc,
+                                            b_sc_estride, Npad, Cm, ldc, c_cap, c_sc, offsets, E, max_rows, N, K, s,
+                                            0, split);
+    if (e != hipSuccess || cfg != kTileMixed) return e;
+    return run_mx<MxLarge, EPI>(A, a_kstride, a_rstride, a_rows, a_sc, a_sc_rows, B, strideB, b_sc, b_sc_estride,
+                                Npad, Cm, ldc, c_cap, c_sc, offsets, E, max_rows, N, K, s, split, INT_MAX);
 }
 
 template <class C>
@@ -482,8 +521,8 @@ hipError_t launch_ffn_up_mx(const void* xq, const void* xs, long x_rows, const i
                             const int32_t* offsets, int E, int max_rows, const uint8_t* W1q, const uint8_t* W1s, int H,
                             int F, void* hq, void* hs, long cap, hipStream_t s) {
     // A: row-major token codes xq[x_rows][H] gathered through row_token, scales [H/128][x_rows][4]
-    return run_mx<MxLarge, 3>(xq, dma::kMxBK, H, row_token, xs, x_rows, W1q, mx_weight_bytes(1, H, F), W1s,
-                              mx_weight_scale_bytes(1, H, F), F, hq, 0, cap, hs, offsets, E, max_rows, F, H, s);
+    return run_mx_cfg<3>(xq, dma::kMxBK, H, row_token, xs, x_rows, W1q, mx_weight_bytes(1, H, F), W1s,
+                         mx_weight_scale_bytes(1, H, F), F, hq, 0, cap, hs, offsets, E, max_rows, F, H, s);
 }
 
 hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const int32_t* offsets, int E, int max_rows,
@@ -492,12 +531,12 @@ hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const in
     // A: the k-blocked h codes [F/64][cap][64] of the W1 launch, scales [F/128][cap][4]
     const long ks = cap * dma::kMxBK;
     if (packed)
-        return run_mx<MxLarge, kEpiPacked24>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
-                                             mx_weight_scale_bytes(1, F, H), H, y, H, cap, nullptr, offsets, E,
-                                             max_rows, H, F, s);
-    return run_mx<MxLarge, kEpiF32Out>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
-                                       mx_weight_scale_bytes(1, F, H), H, y, H, 0, nullptr, offsets, E, max_rows, H,
-                                       F, s);
+        return run_mx_cfg<kEpiPacked24>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
+                                        mx_weight_scale_bytes(1, F, H), H, y, H, cap, nullptr, offsets, E, max_rows,
+                                        H, F, s);
+    return run_mx_cfg<kEpiF32Out>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
+                                  mx_weight_scale_bytes(1, F, H), H, y, H, 0, nullptr, offsets, E, max_rows, H, F,
+                                  s);
 }
 
 TileCfg choose_tile(long rows, int groups) {
