@@ -532,6 +532,8 @@ def main():
         f8 = fp8_times("decode", max(args.steps, 50), max(args.stage_reps, 100))
         line["decode_fp8_experts"] = {k_: f8[k_] for k_ in ("forward_ms", "tokens_per_s", "grouped_ffn_ms",
                                                              "weight_bytes", "weight_stream_gbs")}
+        mx = mx_times("decode", max(args.steps, 50), max(args.stage_reps, 100))
+        line["decode_mxfp8_experts"] = {k_: mx[k_] for k_ in ("forward_ms", "tokens_per_s", "grouped_ffn_ms")}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle) ...")
         line["cpu_baseline"] = cpu_baseline("prefill")
