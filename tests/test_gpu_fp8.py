@@ -5,8 +5,8 @@ with the dequantised weights.
 Bar: codes and scales bit-exact (codes unpacked from the tiled layout the
 header documents, padding columns zero); y_perm and y within 2e-2 * rms of
 the oracle's layer on the oracle's own dequantised weights; routing arrays
-bit-exact; the one-call path within 2^-15 * max|y_perm| of the step-wise path
-(its y_perm is kept as 24-bit floats).
+bit-exact; the one-call path within 2^-10 * max|y_perm| of the step-wise path
+(its y_perm is kept as block-scaled fp16).
 """
 import numpy as np
 import pytest
@@ -174,7 +174,7 @@ def test_fp8_layer_small(dev, over):
     _check_y(y_perm[:A].double().cpu().numpy(), ref.y_perm)
     _check_y(y_steps.double().cpu().numpy(), ref.y)
     _check_y(y.double().cpu().numpy(), ref.y)
-    bound = 2.0 ** -15 * float(y_perm[:A].abs().max()) if A else 0.0
+    bound = 2.0 ** -10 * float(y_perm[:A].abs().max()) if A else 0.0  # block-scaled fp16 y_perm
     assert float((y - y_steps).abs().max()) <= bound
 
 

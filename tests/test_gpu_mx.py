@@ -14,7 +14,7 @@ Bar:
   GPU's code must be one that the bound interval rounds to;
 * y_perm and y within 2e-2 * rms of the oracle's MX layer, widened only by
   the effect of those validated neighbouring codes through W2;
-* the one-call path within 2^-15 * max|y_perm| of the step-wise path, and
+* the one-call path within 2^-10 * max|y_perm| of the step-wise path, and
   reruns bit-identical.
 """
 import numpy as np
@@ -173,8 +173,8 @@ def _validate_layer(dev, I, tokens=None):
     torch.cuda.synchronize()
     assert torch.equal(y, y2)  # deterministic
     A = int(off[-1].item())
-    # the one-call path keeps y_perm as 24-bit floats: within 2^-15 * max|y_perm| of the step-wise result
-    assert float((y - y_steps).abs().max()) <= 2.0 ** -15 * float(y_perm[:A].abs().max())
+    # the one-call path keeps y_perm as block-scaled fp16: within 2^-10 * max|y_perm| of the step-wise result
+    assert float((y - y_steps).abs().max()) <= 2.0 ** -10 * float(y_perm[:A].abs().max())
 
     r = oracle.route(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.k, I.drop)
     disp = oracle.dispatch(r.ids, r.keep, I.E)

@@ -146,12 +146,12 @@ def test_small_layers(dev, name, over):
     check_y(g["y_perm"][:A].double().cpu().numpy(), ref.y_perm)
     check_y(g["y"].double().cpu().numpy(), ref.y)
     # the one-call path: same bar against the oracle, and against the step-wise path within the one extra
-    # rounding it may take (y_perm kept as 24-bit floats inside moe_forward: relative error <= 2^-16 per value,
-    # routing weights summing to 1; the factor 2 covers the fp32 accumulation)
+    # rounding it may take (y_perm kept as block-scaled fp16 inside moe_forward: error <= 2^-11 of the value's
+    # magnitude, routing weights summing to 1; the factor 2 covers the fp32 accumulation)
     y2 = moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], I.k, I.drop, W1s=d["W1s"], W2s=d["W2s"])
     torch.cuda.synchronize()
     check_y(y2.double().cpu().numpy(), ref.y)
-    bound = 2.0 ** -15 * float(g["y_perm"][:A].abs().max()) if A else 0.0
+    bound = 2.0 ** -10 * float(g["y_perm"][:A].abs().max()) if A else 0.0
     assert float((y2 - g["y"]).abs().max()) <= bound
 
 
@@ -253,8 +253,8 @@ def test_permute_oracle_fed(dev, T, E):
 
 @pytest.mark.parametrize("T,H,F,E,k", [
     (256, 128, 64, 16, 4),    # register-staged grouped FFN, fp32 y_perm
-    (600, 256, 256, 4, 2),    # direct-to-LDS large tiles, k-blocked h, 24-bit y_perm planes
-    (40, 256, 256, 16, 4),    # weight-streaming tiles, 24-bit y_perm planes
+    (600, 256, 256, 4, 2),    # direct-to-LDS large tiles, k-blocked h, block-scaled fp16 y_perm
+    (40, 256, 256, 16, 4),    # weight-streaming tiles, block-scaled fp16 y_perm
 ])
 def test_bf16_output_and_determinism(dev, T, H, F, E, k):
     I = gen.make_inputs("tiny", T=T, H=H, F=F, E=E, k=k, dtype="bf16", seed=93)
@@ -285,9 +285,9 @@ def test_full_workload(dev, name, nsample):
                         topk_ids=ids, topk_w=w)
     g = run_steps(d, I, dev)
     assert torch.equal(g["ids"], ids)
-    # moe_forward keeps y_perm as 24-bit floats: within 2^-15 * max|y_perm| of the step-wise (fp32 y_perm) result
+    # moe_forward keeps y_perm as block-scaled fp16: within 2^-10 * max|y_perm| of the step-wise (fp32 y_perm) result
     A = int(g["off"][-1].item())
-    assert float((g["y"] - y).abs().max()) <= 2.0 ** -15 * float(g["y_perm"][:A].abs().max())
+    assert float((g["y"] - y).abs().max()) <= 2.0 ** -10 * float(g["y_perm"][:A].abs().max())
     r = oracle.route(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.k, I.drop)
     dref = oracle.dispatch(r.ids, r.keep, I.E)
     check_routing(g, r, dref, I.x)

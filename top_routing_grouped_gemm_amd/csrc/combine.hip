@@ -91,42 +91,46 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
     }
 }
 
-// 24-bit planes: each thread owns 8 consecutive columns, read as one 16-byte
-// load of their upper halves and one 8-byte load of their low bytes per slot
-// (wider requests than the 4-column form; the same fmaf sequence per value).
+// Block-scaled fp16 y_perm (the W2 epilogue of moe_forward): each thread owns
+// 8 consecutive columns, inside one 32-column scale block, read per slot as
+// one 16-byte load of their fp16 values and one byte of the block's power-of-
+// two exponent s; v = fp16 * 2^s exactly in fp32, then the same fmaf sequence
+// per value as the fp32 form.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_packed_kernel(const u32x4* __restrict__ hi, const u32x2* __restrict__ lo,
-                                                             const int32_t* __restrict__ inv,
-                                                             const float* __restrict__ w,
-                                                             const float4* __restrict__ ysh, int H8, int k,
-                                                             void* __restrict__ y) {
+__global__ __launch_bounds__(256) void combine_f16s_kernel(const u32x4* __restrict__ vals,
+                                                           const int8_t* __restrict__ scales,
+                                                           const int32_t* __restrict__ inv,
+                                                           const float* __restrict__ w,
+                                                           const float4* __restrict__ ysh, int H8, int k,
+                                                           void* __restrict__ y) {
     const long t = blockIdx.x;
+    const int H32 = H8 / 4;  // scale bytes per row
     for (int c = threadIdx.x; c < H8; c += 256) {
         float a[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[i] = 0.0f;
         for (int j0 = 0; j0 < k; j0 += 8) {
             u32x4 vh[8];
-            u32x2 vl[8];
+            int sc[8];
             float ww[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = j0 + u;
                 const int r = j < k ? inv[t * k + j] : -1;
                 ww[u] = r >= 0 ? w[t * k + j] : 0.0f;
-                const long g = (long)(r >= 0 ? r : 0) * H8 + c;
+                const long rr = r >= 0 ? r : 0;
                 // each y_perm value is read exactly once: non-temporal loads
-                vh[u] = r >= 0 ? __builtin_nontemporal_load(hi + g) : u32x4{0u, 0u, 0u, 0u};
-                vl[u] = r >= 0 ? __builtin_nontemporal_load(lo + g) : u32x2{0u, 0u};
+                vh[u] = r >= 0 ? __builtin_nontemporal_load(vals + rr * H8 + c) : u32x4{0u, 0u, 0u, 0u};
+                sc[u] = r >= 0 ? (int)scales[rr * H32 + c / 4] : 0;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (j0 + u < k && ww[u] != 0.0f) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const uint32_t h16 = (vh[u][i >> 1] >> (16 * (i & 1))) & 0xffffu;
-                        const uint32_t l8 = (vl[u][i >> 2] >> (8 * (i & 3))) & 0xffu;
-                        a[i] = fmaf(ww[u], __uint_as_float((h16 << 16) | (l8 << 8)), a[i]);
+                        const uint16_t hb = (uint16_t)((vh[u][i >> 1] >> (16 * (i & 1))) & 0xffffu);
+                        const float v = ldexpf((float)__builtin_bit_cast(_Float16, hb), sc[u]);
+                        a[i] = fmaf(ww[u], v, a[i]);
                     }
                 }
             }
@@ -158,13 +162,13 @@ hipError_t combine(const void* y_perm, long lo_off, const int32_t* inv, const fl
                    int H, int k, Dtype out_dt, void* y, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if constexpr (PACKED) {
-        const u32x4* hi = (const u32x4*)y_perm;
-        const u32x2* lo = (const u32x2*)((const uint8_t*)y_perm + lo_off);
+        const u32x4* vals = (const u32x4*)y_perm;
+        const int8_t* sc = (const int8_t*)((const uint8_t*)y_perm + lo_off);
         if (out_dt == kBF16)
-            hipLaunchKernelGGL((combine_packed_kernel<true>), dim3(T), dim3(256), 0, s, hi, lo, inv, w,
+            hipLaunchKernelGGL((combine_f16s_kernel<true>), dim3(T), dim3(256), 0, s, vals, sc, inv, w,
                                (const float4*)y_shared, H / 8, k, y);
         else
-            hipLaunchKernelGGL((combine_packed_kernel<false>), dim3(T), dim3(256), 0, s, hi, lo, inv, w,
+            hipLaunchKernelGGL((combine_f16s_kernel<false>), dim3(T), dim3(256), 0, s, vals, sc, inv, w,
                                (const float4*)y_shared, H / 8, k, y);
         return hipGetLastError();
     }

@@ -181,6 +181,21 @@ __device__ __forceinline__ float dpp_swap2(float v) {  // lane i <- lane i^2 wit
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
+// Largest |v| over the 32 columns of one row after quad_transpose: the lanes
+// holding them share l % 4 and l / 32 (8 quads). Rotations by 4 and 8 lanes
+// inside each 16-lane DPP row, then an exchange with the other 16-lane row of
+// the same 32-lane half (permlane16 swap); all of it on the VALU, no LDS
+// round trips. Compared as integers: non-negative floats order like their
+// bit patterns.
+__device__ __forceinline__ float row32_absmax(const float (&v)[4]) {
+    int b = max(max(__float_as_int(v[0]) & 0x7fffffff, __float_as_int(v[1]) & 0x7fffffff),
+                max(__float_as_int(v[2]) & 0x7fffffff, __float_as_int(v[3]) & 0x7fffffff));
+    b = max(b, __builtin_amdgcn_mov_dpp(b, 0x124, 0xF, 0xF, false));  // row_ror:4
+    b = max(b, __builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, false));  // row_ror:8
+    const auto s = __builtin_amdgcn_permlane16_swap((unsigned)b, (unsigned)b, false, false);
+    return __int_as_float(max((int)s[0], (int)s[1]));
+}
+
 // 4x4 transpose across the 4 lanes of a quad: on entry lane m holds column m
 // (v[r] = M[r][m]); on exit it holds row m (v[c] = M[m][c]).
 __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
@@ -213,44 +228,55 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
 // contiguous run instead of 64-byte pieces of separate rows. Rows past the
 // group are dropped by an explicit out-of-range offset in that layout.
 //
-// EPI 2 (fp32 result as a 24-bit float): the fp32 bits rounded to their top 24
-// (sign, exponent, 15 mantissa bits; relative error <= 2^-16) go to two planes,
-// the upper 16 bits at C[r*ldc + n] (2-byte elements) and the next 8 bits at
-// byte (C + c_cap*ldc*2)[r*ldc + n], c_cap being the row capacity: 3 bytes per
-// value instead of 4 for a result that is read once more.
+// EPI 4 (fp32 result as block-scaled fp16, for a result read once more): per
+// row and 32-column block a power of two 2^s puts the block's largest
+// magnitude in [2^14, 2^15) (s = floor(log2 max) - 14, clamped to
+// [-127, 127]; s = 0 for an all-zero block); the values v * 2^-s rounded to
+// fp16 (nearest even; relative error <= 2^-11, no overflow for any finite
+// input) go to C[r*ldc + n] (2-byte elements) and s as a signed byte to
+// (C + c_cap*ldc*2)[r*(ldc/32) + n/32], c_cap being the row capacity:
+// 2 + 1/32 bytes per value instead of 4 (N % 32 == 0, ldc % 32 == 0).
 template <int TM, int TN, int WTM, int WTN, int EPI>
 __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, long ldc, long c_cap, int rb, int re,
                                              int n0, int N, int wm, int wn) {
-    if constexpr (EPI == 2) {
+    if constexpr (EPI == 4) {
         const int l = lane_id();
-        const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
+        const int lds = (int)(ldc / 32);  // scale bytes per row
+        const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
             (uint8_t*)C + ((long)rb * ldc + n0) * 2, (short)0, (int)(((long)(re - rb) * ldc - n0) * 2), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
-            (uint8_t*)C + c_cap * ldc * 2 + (long)rb * ldc + n0, (short)0, (int)((long)(re - rb) * ldc - n0),
+        const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+            (uint8_t*)C + c_cap * ldc * 2 + (long)rb * lds + n0 / 32, (short)0, (int)((long)(re - rb) * lds - n0 / 32),
             0x00020000);
         const int c0 = (l & 31) & ~3, m = l & 3;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int jj = 0; jj < TN; ++jj) {
-                const int colrel = wn * WTN + jj * 32 + c0;
-                const bool col_ok = n0 + colrel < N;
+                const int blk = wn * WTN + jj * 32;  // first column of this 32-column block, tile-relative
+                const bool col_ok = n0 + blk + c0 < N;  // this lane's 4 columns (N % 32 == 0: whole blocks)
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     float v[4] = {acc[i][jj][4 * p], acc[i][jj][4 * p + 1], acc[i][jj][4 * p + 2],
                                   acc[i][jj][4 * p + 3]};
                     quad_transpose(v);
+                    if (!col_ok) v[0] = v[1] = v[2] = v[3] = 0.0f;
                     const int rowrel = wm * WTM + i * 32 + 8 * p + 4 * (l >> 5) + m;
-                    const int e = rowrel * (int)ldc + colrel;  // element offset within the tile's rows
-                    uint32_t u[4];
+                    const float am = row32_absmax(v);
+                    const int ex = (int)((__float_as_uint(am) >> 23) & 0xffu);
+                    const int sc = am > 0.0f ? min(127, max(-127, ex - 127 - 14)) : 0;
+                    uint32_t hbits[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) u[q] = __float_as_uint(v[q]) + 0x80u;  // round to 24 bits
+                    for (int q = 0; q < 4; ++q) {
+                        const _Float16 h = (_Float16)ldexpf(v[q], -sc);
+                        hbits[q] = (uint32_t)__builtin_bit_cast(uint16_t, h);
+                    }
                     typedef __attribute__((ext_vector_type(2))) unsigned u2;
-                    const u2 hi = {(u[0] >> 16) | (u[1] & 0xffff0000u), (u[2] >> 16) | (u[3] & 0xffff0000u)};
-                    const uint32_t lo = ((u[0] >> 8) & 0xffu) | (((u[1] >> 8) & 0xffu) << 8) |
-                                        (((u[2] >> 8) & 0xffu) << 16) | (((u[3] >> 8) & 0xffu) << 24);
-                    __builtin_amdgcn_raw_buffer_store_b64(hi, rs_hi, col_ok ? e * 2 : 0x7ffffff0, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b32(lo, rs_lo, col_ok ? e : 0x7ffffff0, 0, 0);
+                    const u2 pk = {hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16)};
+                    const int e = rowrel * (int)ldc + blk + c0;  // element offset within the tile's rows
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, rs_v, col_ok ? e * 2 : 0x7ffffff0, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)sc, rs_s,
+                                                         (col_ok && c0 == 0) ? rowrel * lds + blk / 32 : 0x7ffffff0,
+                                                         0, 0);
                 }
             }
         return;

@@ -72,10 +72,7 @@ __device__ __forceinline__ void store_tile_mx(f32x16 (&acc)[TM][TN], uint8_t* C,
                 quad_transpose(v);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) v[q] = silu_f32(v[q]);
-                float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-                am = fmaxf(am, __shfl_xor(am, 4));   // the 8 quads of this row's 32-column block
-                am = fmaxf(am, __shfl_xor(am, 8));
-                am = fmaxf(am, __shfl_xor(am, 16));
+                const float am = row32_absmax(v);  // this row's 32-column block
                 const int x = mx_exponent(am);
                 const uint32_t codes = mx_codes4(v[0], v[1], v[2], v[3], x);
                 const int col = colw + jj * 32 + c0;
@@ -97,7 +94,7 @@ __device__ __forceinline__ void store_tile_mx(f32x16 (&acc)[TM][TN], uint8_t* C,
 //      bytes of the 128-k pair of blocks.
 //   B: expert e's codes at B + e*strideB as 8 KiB tiles [Npad/128][K/64][128 n][64 k];
 //      scales b_sc + e*b_sc_estride + ((kb/2)*Npad + n)*4.
-//   EPI 1 / 2: fp32 / 24-bit planes as store_tile32 (ldc, c_cap); EPI 3: SiLU,
+//   EPI 1 / 4: fp32 / block-scaled fp16 as store_tile32 (ldc, c_cap); EPI 3: SiLU,
 //   MX codes to the k-blocked C[N/64][c_cap][64] and scale dwords to c_sc[N/128][c_cap][4].
 // Requirements (host): K % 128 == 0, K >= 128, N % 128 == 0.
 template <int BM, int BN, int NS, int WM, int WN, int EPI>
@@ -260,10 +257,7 @@ __device__ __forceinline__ void store_tile_mx32(f32x16 (&acc)[TM][1], uint8_t* C
             quad_transpose(v);
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = silu_f32(v[q]);
-            float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-            am = fmaxf(am, __shfl_xor(am, 4));  // the 8 quads of this row's 32-column block
-            am = fmaxf(am, __shfl_xor(am, 8));
-            am = fmaxf(am, __shfl_xor(am, 16));
+            const float am = row32_absmax(v);  // this row's 32-column block
             const int x = mx_exponent(am);
             const uint32_t codes = mx_codes4(v[0], v[1], v[2], v[3], x);
             const int col = colw + c0;

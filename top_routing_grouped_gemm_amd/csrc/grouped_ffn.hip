@@ -9,7 +9,7 @@
 // prefill many.
 //
 //   up:   h[r]      = silu(x_perm[r] @ W1[e])   (SiLU fused in the epilogue)
-//   down: y_perm[r] = h[r] @ W2[e]              (fp32 out, or 24-bit planes)
+//   down: y_perm[r] = h[r] @ W2[e]              (fp32 out, or block-scaled fp16)
 //
 // Scheduling: the M-tiles of all experts form one ragged sequence (expert e
 // contributes ceil(count_e / BM) tiles); each workgroup takes one (M-tile,
@@ -82,7 +82,7 @@ __device__ __forceinline__ bool locate(const int32_t* __restrict__ offsets, int 
     return find_tile<BM>(offsets, E, mt, e, rb, re);
 }
 
-enum { kEpiSiluOut = 0, kEpiF32Out = 1, kEpiPacked24 = 2 };
+enum { kEpiSiluOut = 0, kEpiF32Out = 1, kEpiScaled16 = 4 };
 
 template <int BM, int BN, int BK, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(
@@ -469,7 +469,7 @@ long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt) {
 }
 
 bool ffn_down_packs(TileCfg cfg, int F, int H, Dtype dt) {
-    if (dt != kBF16) return false;
+    if (dt != kBF16 || H % 32 != 0) return false;  // whole 32-column scale blocks
     if (cfg == kTileM128) return dma_ok<DmaLarge>(F, H, H, F);
     if (cfg == kTileM16) return dma_ok<DmaStream>(F, H, H, F);
     if (cfg == kTileMixed) return dma_ok<DmaLarge>(F, H, H, F) && dma_ok<DmaStream>(F, H, H, F);
@@ -481,19 +481,19 @@ hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, 
     const long sb = (long)F * H;
     if (cfg == kTileM128) {
         if (h_cap > 0)
-            return run_dma<DmaLarge, kEpiPacked24>(h, 32, h_cap, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0,
+            return run_dma<DmaLarge, kEpiScaled16>(h, 32, h_cap, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0,
                                                    max_rows, H, F, s);
-        return run_dma<DmaLarge, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
+        return run_dma<DmaLarge, kEpiScaled16>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
                                                H, F, s);
     }
     if (cfg == kTileMixed) {
-        const hipError_t e = run_dma<DmaStream, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets,
+        const hipError_t e = run_dma<DmaStream, kEpiScaled16>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets,
                                                               E, 0, max_rows, H, F, s, 0, kStreamRows);
         if (e != hipSuccess) return e;
-        return run_dma<DmaLarge, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
+        return run_dma<DmaLarge, kEpiScaled16>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
                                                H, F, s, kStreamRows, INT_MAX);
     }
-    return run_dma<DmaStream, kEpiPacked24>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows, H,
+    return run_dma<DmaStream, kEpiScaled16>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows, H,
                                             F, s);
 }
 
@@ -510,7 +510,7 @@ hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int
                                hipStream_t s) {
     const long strideB = fp8_weight_bytes(1, F, H);
     if (packed)
-        return run_fp8_cfg<kEpiPacked24>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, cap, offsets, E, max_rows, H, F,
+        return run_fp8_cfg<kEpiScaled16>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, cap, offsets, E, max_rows, H, F,
                                          s);
     return run_fp8_cfg<kEpiF32Out>(cfg, h, F, nullptr, W2q, strideB, s2, y, H, 0, offsets, E, max_rows, H, F, s);
 }
@@ -531,7 +531,7 @@ hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const in
     // A: the k-blocked h codes [F/64][cap][64] of the W1 launch, scales [F/128][cap][4]
     const long ks = cap * dma::kMxBK;
     if (packed)
-        return run_mx_cfg<kEpiPacked24>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
+        return run_mx_cfg<kEpiScaled16>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,
                                         mx_weight_scale_bytes(1, F, H), H, y, H, cap, nullptr, offsets, E, max_rows,
                                         H, F, s);
     return run_mx_cfg<kEpiF32Out>(hq, ks, dma::kMxBK, nullptr, hs, cap, W2q, mx_weight_bytes(1, F, H), W2s,

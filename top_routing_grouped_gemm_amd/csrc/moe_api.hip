@@ -90,7 +90,7 @@ FwdLayout fwd_layout(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) 
 }
 
 // Workspace of moe_forward_mxfp8: routing and dispatch maps as in moe_forward,
-// the MX codes and scales of x and of the SiLU output, and the 24-bit planes of y_perm.
+// the MX codes and scales of x and of the SiLU output, and y_perm in block-scaled fp16.
 struct MxLayout {
     size_t ids, w, offsets, inv, row_token, partial, route, xq, xs, hq, hs, y, total;
 };
@@ -114,7 +114,7 @@ MxLayout mx_layout(int T, int H, int F, int E, int k) {
     take(L.xs, (size_t)(H / 128) * T * 4);
     take(L.hq, TK * F);
     take(L.hs, (size_t)(F / 128) * TK * 4);
-    take(L.y, TK * H * 3);
+    take(L.y, TK * H * 2 + TK * (H / 32));
     L.total = off;
     return L;
 }
@@ -145,7 +145,7 @@ int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, in
 }
 
 // row_token != NULL: the W1 launch gathers rows of x through row_token instead of reading x_perm.
-// packed: y_perm is written as the two 24-bit planes of ffn_down_packs (the caller checked that it applies).
+// packed: y_perm is written in the block-scaled fp16 form of ffn_down_packs (the caller checked that it applies).
 int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* offsets, const void* W1, const void* W2,
                 int T, int H, int F, int E, int k, moe_dtype_t dt, float* y_perm, const void* x, const void* W1s,
                 const void* W2s, int Fs, float* y_shared, void* ws, bool packed, hipStream_t s) {
@@ -399,7 +399,7 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
     void* route_ws = base + L.route;
 
     // direct-to-LDS shapes: the W1 launch gathers x rows itself (x_perm is never written) and the W2 launch
-    // writes y_perm as 24-bit floats (the combine reads 3 bytes per value instead of 4)
+    // writes y_perm as block-scaled fp16 (the combine reads 2 + 1/32 bytes per value instead of 4)
     const moe::TileCfg cfg = moe::choose_tile((long)T * k, E);
     const bool gather = moe::ffn_up_gathers(cfg, H, F, (Dtype)dt);
     const bool packed = moe::ffn_down_packs(cfg, F, H, (Dtype)dt);
@@ -474,7 +474,7 @@ int moe_forward_fp8(const void* x, const void* Wr, const float* bias, const uint
     void* h = base + L.ffn + ffn_layout(T, F, k, 0, MOE_BF16).h;
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
-    // the W1 launch gathers x rows through row_token (no permuted copy); the W2 launch writes 24-bit y_perm planes
+    // the W1 launch gathers x rows through row_token (no permuted copy); the W2 launch writes block-scaled fp16 y_perm
     MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, moe::kBF16, ids, w, base + L.route, stream));
     if ((st = enqueue_permute(x, ids, w, T, H, E, k, MOE_BF16, nullptr, off, row_token, iv, partial, false,
                               stream)) != MOE_OK)

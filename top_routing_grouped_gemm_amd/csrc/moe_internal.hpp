@@ -67,9 +67,10 @@ hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fix
 // Row capacity for the k-blocked h (the large direct-to-LDS shape with bf16
 // and F % 32 == 0), or 0 for row-major.
 long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt);
-// Whether the W2 launch can write y_perm as a 24-bit float in two planes (the
-// direct-to-LDS shapes): upper 16 bits of each fp32 value at
-// planes[r*H + n] (2 bytes), next 8 bits at ((uint8_t*)planes + cap*H*2)[r*H + n].
+// Whether the W2 launch can write y_perm as block-scaled fp16 (the
+// direct-to-LDS shapes, H % 32 == 0): fp16 values of v * 2^-s at
+// planes[r*H + n] (2 bytes), the signed exponent s of row r's 32-column block
+// at ((int8_t*)planes + cap*H*2)[r*(H/32) + n/32]; cap*H*(2 + 1/32) bytes.
 bool ffn_down_packs(TileCfg cfg, int F, int H, Dtype dt);
 hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, int max_rows, const void* W2, int F,
                                   int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s);
@@ -87,8 +88,8 @@ hipError_t launch_quantize_fp8(const void* W, int E, int K, int N, Dtype dt, uin
                                hipStream_t s);
 // Grouped FFN on fp8 weights (bf16 activations): W1 [E][H][F] and W2 [E][F][H]
 // as tiled codes with per-column scales. a_rows != NULL gathers the W1 A rows
-// from x through the row -> token map; packed: y as the 24-bit planes of
-// ffn_down_packs, else fp32 y[rows][H].
+// from x through the row -> token map; packed: y in the block-scaled fp16 form
+// of ffn_down_packs, else fp32 y[rows][H].
 bool ffn_fp8_ok(int H, int F);
 hipError_t launch_ffn_up_fp8(const void* A, const int32_t* a_rows, const int32_t* offsets, int E, int max_rows,
                              const uint8_t* W1q, const float* s1, int H, int F, TileCfg cfg, void* h, hipStream_t s);
@@ -100,8 +101,8 @@ hipError_t launch_ffn_down_fp8(const void* h, const int32_t* offsets, int E, int
 // [R][H] and scales [H/128][R][4]. Weights [E][K][N] to code tiles (mx_weight_bytes) + scales
 // (mx_weight_scale_bytes). The W1 launch gathers row-major token codes
 // xq[x_rows][H] through row_token and writes SiLU(h) as k-blocked MX codes hq[F/64][cap][64] + scales
-// hs[F/128][cap][4]; the W2 launch writes y as fp32 [cap][H] or the 24-bit
-// planes (packed). H, F multiples of 128.
+// hs[F/128][cap][4]; the W2 launch writes y as fp32 [cap][H] or in the
+// block-scaled fp16 form (packed). H, F multiples of 128.
 long mx_weight_bytes(int E, int K, int N);
 long mx_weight_scale_bytes(int E, int K, int N);
 hipError_t launch_quantize_mx_rows(const void* x, long R, int H, Dtype dt, uint8_t* xq, uint8_t* xs, hipStream_t s);
@@ -115,7 +116,7 @@ hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const in
                               const uint8_t* W2q, const uint8_t* W2s, int F, int H, bool packed, void* y,
                               hipStream_t s);
 
-// y_perm given as the two planes of ffn_down_packs (cap = row capacity).
+// y_perm given in the block-scaled fp16 form of ffn_down_packs (cap = row capacity).
 hipError_t launch_combine_packed(const void* y_planes, long cap, const int32_t* inv, const float* w,
                                  const float* y_shared, int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* w, const float* y_shared,
