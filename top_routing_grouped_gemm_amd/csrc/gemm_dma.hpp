@@ -248,19 +248,24 @@ __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, lon
             (uint8_t*)C + c_cap * ldc * 2 + (long)rb * lds + n0 / 32, (short)0, (int)((long)(re - rb) * lds - n0 / 32),
             0x00020000);
         const int c0 = (l & 31) & ~3, m = l & 3;
+        // a wave spanning whole 128-column groups (n0 and ldc multiples of 128) gathers the 4 scale bytes
+        // of each group in a register and stores them as one aligned 4-byte word; otherwise byte stores
+        constexpr bool kWord = TN % 4 == 0;
+        const bool word = kWord && ldc % 128 == 0 && n0 % 128 == 0;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int jj = 0; jj < TN; ++jj) {
-                const int blk = wn * WTN + jj * 32;  // first column of this 32-column block, tile-relative
-                const bool col_ok = n0 + blk + c0 < N;  // this lane's 4 columns (N % 32 == 0: whole blocks)
+            for (int p = 0; p < 4; ++p) {
+                const int rowrel = wm * WTM + i * 32 + 8 * p + 4 * (l >> 5) + m;
+                uint32_t sw = 0;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
+                for (int jj = 0; jj < TN; ++jj) {
+                    const int blk = wn * WTN + jj * 32;     // first column of this 32-column block, tile-relative
+                    const bool col_ok = n0 + blk + c0 < N;  // this lane's 4 columns (N % 32 == 0: whole blocks)
                     float v[4] = {acc[i][jj][4 * p], acc[i][jj][4 * p + 1], acc[i][jj][4 * p + 2],
                                   acc[i][jj][4 * p + 3]};
                     quad_transpose(v);
                     if (!col_ok) v[0] = v[1] = v[2] = v[3] = 0.0f;
-                    const int rowrel = wm * WTM + i * 32 + 8 * p + 4 * (l >> 5) + m;
                     const float am = row32_absmax(v);
                     const int ex = (int)((__float_as_uint(am) >> 23) & 0xffu);
                     const int sc = am > 0.0f ? min(127, max(-127, ex - 127 - 14)) : 0;
@@ -274,9 +279,18 @@ __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, lon
                     const u2 pk = {hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16)};
                     const int e = rowrel * (int)ldc + blk + c0;  // element offset within the tile's rows
                     __builtin_amdgcn_raw_buffer_store_b64(pk, rs_v, col_ok ? e * 2 : 0x7ffffff0, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)sc, rs_s,
-                                                         (col_ok && c0 == 0) ? rowrel * lds + blk / 32 : 0x7ffffff0,
-                                                         0, 0);
+                    if (kWord) sw |= (uint32_t)(uint8_t)(int8_t)sc << (8 * (jj & 3));
+                    if (!word)
+                        __builtin_amdgcn_raw_buffer_store_b8(
+                            (uint8_t)(int8_t)sc, rs_s, (col_ok && c0 == 0) ? rowrel * lds + blk / 32 : 0x7ffffff0, 0,
+                            0);
+                    if (kWord && (jj & 3) == 3) {
+                        const int blk0 = blk - 96;  // the group's first block
+                        if (word)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                sw, rs_s, (c0 == 0 && n0 + blk0 < N) ? rowrel * lds + blk0 / 32 : 0x7ffffff0, 0, 0);
+                        sw = 0;
+                    }
                 }
             }
         return;
