@@ -50,7 +50,7 @@ def test_workspace_queries(lib):
     assert n >= T * k * (H * 2 + H * 4 + F * 2)
     assert lib.moe_workspace_bytes(T, H, F, E, k, 4096, bf16) > n  # shared expert adds h_sh, y_sh
     assert lib.moe_workspace_bytes(T, H, F, E, k, 0, f32) > n
-    assert lib.moe_permute_workspace_bytes(T, E, k) == ((T * k + 255) // 256) * E * 4
+    assert lib.moe_permute_workspace_bytes(T, E, k) == ((T * k + 1023) // 1024) * E * 4  # per-chunk counts, 1024 slots a chunk
     assert lib.moe_ffn_workspace_bytes(T, F, E, k, 0, bf16) >= T * k * F * 2
     for bad in [(0, H, F, E, k), (T, 0, F, E, k), (T, H, 0, E, k), (T, H, F, 0, k), (T, H, F, E, 0),
                 (T, H, F, E, E + 1), (T, 12, F, E, k), (T, H, F, 2048, k), (T, H, F, 64, 40)]:
