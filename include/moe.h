@@ -257,6 +257,15 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w,
  * [E+1] and inv [T,k] may be NULL; when given they receive the same values
  * the step-wise calls would produce. ws: at least
  * moe_workspace_bytes(T,H,F,E,k,Fs,dt) bytes.
+ *
+ * Precision: when dt = MOE_BF16, H % 32 == 0 and the library runs the
+ * routed W2 product on its direct-to-LDS GEMM shapes (picked from the rows
+ * per expert and the sizes), the routed y_perm stays inside the workspace as
+ * block-scaled fp16: per row and 32 columns a power of two puts the block
+ * maximum in [2^14, 2^15), and each value is rounded to fp16 (error <= 2^-11
+ * of its magnitude). y then differs from the step-wise (fp32 y_perm) result
+ * by at most 2^-11 * max|y_perm| * sum_j topk_w[t,j] plus fp32 accumulation;
+ * everything else is as in the step-wise calls.
  */
 int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1, const void* W2,
                 const void* W1s, const void* W2s, int Fs, int T, int H, int F, int E, int k,
