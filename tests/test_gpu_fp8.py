@@ -13,6 +13,7 @@ import pytest
 
 import gen
 import oracle
+from tests.scaled16 import scaled16_bound
 
 torch = pytest.importorskip("torch")
 moe = pytest.importorskip("top_routing_grouped_gemm_amd")
@@ -176,6 +177,9 @@ def test_fp8_layer_small(dev, over):
     _check_y(y.double().cpu().numpy(), ref.y)
     bound = 2.0 ** -10 * float(y_perm[:A].abs().max()) if A else 0.0  # block-scaled fp16 y_perm
     assert float((y - y_steps).abs().max()) <= bound
+    if I.H % 32 == 0:  # and element by element
+        eb = scaled16_bound(y_perm, A, inv, w, y_steps)
+        assert bool(((y - y_steps).abs().double() <= eb).all()), "one-call y outside the fp16 rounding bound"
 
 
 @pytest.mark.parametrize("name,nsample", [("decode", 8), ("prefill", 6)])

@@ -22,6 +22,7 @@ import pytest
 
 import gen
 import oracle
+from tests.scaled16 import scaled16_bound
 
 torch = pytest.importorskip("torch")
 moe = pytest.importorskip("top_routing_grouped_gemm_amd")
@@ -173,8 +174,12 @@ def _validate_layer(dev, I, tokens=None):
     torch.cuda.synchronize()
     assert torch.equal(y, y2)  # deterministic
     A = int(off[-1].item())
-    # the one-call path keeps y_perm as block-scaled fp16: within 2^-10 * max|y_perm| of the step-wise result
+    # the one-call path keeps y_perm as block-scaled fp16: within 2^-10 * max|y_perm| of the step-wise result,
+    # and within the rounding bound element by element
     assert float((y - y_steps).abs().max()) <= 2.0 ** -10 * float(y_perm[:A].abs().max())
+    if I.H % 32 == 0:
+        eb = scaled16_bound(y_perm, A, inv, w, y_steps)
+        assert bool(((y - y_steps).abs().double() <= eb).all()), "one-call y outside the fp16 rounding bound"
 
     r = oracle.route(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.k, I.drop)
     disp = oracle.dispatch(r.ids, r.keep, I.E)
