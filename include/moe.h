@@ -263,9 +263,10 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w,
  * per expert and the sizes), the routed y_perm stays inside the workspace as
  * block-scaled fp16: per row and 32 columns a power of two puts the block
  * maximum in [2^14, 2^15), and each value is rounded to fp16 (error <= 2^-11
- * of its magnitude). y then differs from the step-wise (fp32 y_perm) result
- * by at most 2^-11 * max|y_perm| * sum_j topk_w[t,j] plus fp32 accumulation;
- * everything else is as in the step-wise calls.
+ * of its magnitude; <= 2^(s-25) for the values under fp16's normal range,
+ * below 2^-28 of the block maximum). y then differs from the step-wise
+ * (fp32 y_perm) result by at most 2^-11 * max|y_perm| * sum_j topk_w[t,j]
+ * plus fp32 accumulation; everything else is as in the step-wise calls.
  */
 int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1, const void* W2,
                 const void* W1s, const void* W2s, int Fs, int T, int H, int F, int E, int k,

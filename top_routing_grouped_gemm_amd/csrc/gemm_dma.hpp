@@ -232,8 +232,9 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
 // row and 32-column block a power of two 2^s puts the block's largest
 // magnitude in [2^14, 2^15) (s = floor(log2 max) - 14, clamped to
 // [-127, 127]; s = 0 for an all-zero block); the values v * 2^-s rounded to
-// fp16 (nearest even; relative error <= 2^-11, no overflow for any finite
-// input) go to C[r*ldc + n] (2-byte elements) and s as a signed byte to
+// fp16 (nearest even; relative error <= 2^-11, absolute <= 2^(s-25) for the
+// values under fp16's normal range; no overflow for any finite input) go to
+// C[r*ldc + n] (2-byte elements) and s as a signed byte to
 // (C + c_cap*ldc*2)[r*(ldc/32) + n/32], c_cap being the row capacity:
 // 2 + 1/32 bytes per value instead of 4 (N % 32 == 0, ldc % 32 == 0).
 template <int TM, int TN, int WTM, int WTN, int EPI>
