@@ -309,6 +309,41 @@ def test_full_workload(dev, name, nsample):
     _say(f"{name}: routing bit-exact over {I.T} tokens; y max-abs/rms {rel:.3e} on {len(toks)} tokens")
 
 
+# ---------------------------------------------- one very large expert --
+def test_group_beyond_32bit_bytes(dev):
+    """One expert holding 131,072 rows of H = 8192: its fp32 y_perm spans 4 GiB, more than a 32-bit byte count
+    measured from the group's first row. Every GEMM epilogue must bound its stores by its own tile's rows; the
+    first tiles of the group (tokens 0..255 among the samples) would otherwise lose or misplace their stores.
+    Step-wise and one-call y are checked against the oracle on sampled tokens (E = 1, k = 1: weight 1). The
+    inputs are seeded torch normals drawn on the device (the shared generator would take a minute here)."""
+    import types
+    T, H, F = 131072, 8192, 64
+    _say(f"case one-group T={T} H={H} F={F}")
+    gdev = torch.Generator(device=dev).manual_seed(131)
+    gcpu = torch.Generator().manual_seed(132)
+    d = {"x": torch.randn((T, H), generator=gdev, device=dev).to(torch.bfloat16),
+         "Wr": (torch.randn((H, 1), generator=gcpu) / H ** 0.5).to(torch.bfloat16).to(dev),
+         "W1": (torch.randn((1, H, F), generator=gcpu) / H ** 0.5).to(torch.bfloat16).to(dev),
+         "W2": (torch.randn((1, F, H), generator=gcpu) / F ** 0.5).to(torch.bfloat16).to(dev),
+         "bias": None, "W1s": None, "W2s": None}
+    I = types.SimpleNamespace(T=T, k=1, E=1, Fs=0, drop=0.0)
+    g = run_steps(d, I, dev)
+    assert bool((g["ids"] == 0).all()) and int(g["off"][-1].item()) == T
+    y1 = moe.moe_forward(d["x"], d["Wr"], None, d["W1"], d["W2"], 1)
+    torch.cuda.synchronize()
+    toks = np.array(sorted({0, 1, 100, 255, 256, 511, 4096, 65535, 65536, 100000, T - 257, T - 1}))
+    sel = torch.from_numpy(toks).to(dev)
+
+    def f64(t):
+        return t.float().double().cpu().numpy()
+
+    W1, W2 = f64(d["W1"][0]), f64(d["W2"][0])
+    _, _, _, yref = oracle.forward_tokens(np.arange(len(toks)), f64(d["x"][sel]), f64(d["Wr"]), np.zeros(1),
+                                          lambda e: W1, lambda e: W2, 1)
+    check_y(g["y"][sel].double().cpu().numpy(), yref)
+    check_y(y1[sel].double().cpu().numpy(), yref)
+
+
 # ------------------------------------------------ no kept assignments --
 def test_nothing_kept(dev):
     """A batch whose every slot is dropped (weight 0) or names no expert: permute keeps no row (all offsets 0,

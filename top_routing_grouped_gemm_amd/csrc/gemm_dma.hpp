@@ -214,7 +214,8 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
     v[3] = o2 ? y3 : r1;
 }
 
-// Writes a workgroup's accumulators for rows [rb, re) and columns n0.. of C:
+// Writes a workgroup's accumulators for rows [rb, re) and columns n0.. of C
+// (re at most rb + the tile's rows, so the byte ranges below stay small):
 // a quad transpose gives each lane 4 adjacent columns of one row, stored with
 // one 16-byte (fp32) or 8-byte (SiLU + bf16) buffer store. Rows past the group
 // and columns past N get an out-of-range offset and are dropped by the buffer
@@ -549,7 +550,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
         }
     }
 
-    store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, wm, wn);
+    // the epilogue's buffer ranges span this tile's rows only (re - rb can exceed 2^31 bytes of C for one
+    // very large group)
+    store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
 }
 
 }  // namespace dma

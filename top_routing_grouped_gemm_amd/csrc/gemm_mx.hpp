@@ -231,8 +231,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mx_kernel(
     if (!active) return;
     if constexpr (EPI == 3)
         store_tile_mx<TM, TN, WTM, WTN>(acc, (uint8_t*)C, c_cap, c_sc, rb, re, n0, N, wm, wn);
-    else
-        store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, wm, wn);
+    else  // buffer ranges over this tile's rows only
+        store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
 }
 
 // EPI 3 for waves of 32 columns: SiLU, one 32-value block per row and wave,
@@ -379,8 +379,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_stream_kernel(
     }
     if constexpr (EPI == 3)
         store_tile_mx32<1>(acc, (uint8_t*)C, c_cap, c_sc, rb, re, n0 + 32 * uwave, N, 0, BM);
-    else
-        store_tile32<1, 1, BM, 32, EPI>(acc, C, ldc, c_cap, rb, re, n0, N, 0, uwave);
+    else  // buffer ranges over this tile's rows only
+        store_tile32<1, 1, BM, 32, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, 0, uwave);
 }
 
 }  // namespace dma
