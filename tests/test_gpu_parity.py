@@ -255,6 +255,40 @@ def test_permute_oracle_fed(dev, T, E):
     check_routing(g, r, dref, I.x)
 
 
+# ---------------------------------------------------------- exact ties --
+@pytest.mark.parametrize("T,E,k", [
+    (512, 16, 4),      # H loop split across workgroups, top-k in the reduction kernel
+    (16384, 16, 4),    # enough token blocks: no split, top-k fused into the router kernel
+    (512, 256, 8),     # four logits per lane
+])
+def test_router_exact_ties(dev, T, E, k):
+    """Experts with identical router columns get bit-identical logits on both sides (each logit is the same
+    ordered sum of the same products); where such a tie straddles the k-th place, the lower expert id must be
+    selected. Tokens whose k-th/(k+1)-th gap is neither exactly 0 (a planted tie) nor clear of fp32 rounding
+    (>= 1e-4) are left out; the test requires some tokens with a tie at the boundary."""
+    H = 256
+    I = gen.make_inputs("tiny", T=T, H=H, F=64, E=E, k=k, dtype="bf16", seed=141 + E)
+    _say(f"case ties T={T} E={E} k={k}")
+    pairs = [(5, 3), (9, 3), (12, 0), (13, 7)] + ([(2 * i + 1, 2 * i) for i in range(8, 64)] if E >= 128 else [])
+    Wr = I.Wr.copy()
+    for dst, src in pairs:
+        Wr[:, dst] = Wr[:, src]
+    ids, w = moe.moe_route(gen.storage_to_torch(I.x, I.dtype).to(dev), gen.storage_to_torch(Wr, I.dtype).to(dev),
+                           None, k)
+    torch.cuda.synchronize()
+    lg = oracle.router_logits(I.f64(I.x), I.f64(Wr))
+    for dst, src in pairs:
+        lg[:, dst] = lg[:, src]  # exact ties in fp64 too, whatever the matrix product's summation order
+    ids_ref, gap = oracle.select_topk(lg, k)
+    w_ref, _ = oracle.selection_weights(lg, ids_ref)
+    tied = gap == 0.0
+    use = tied | (gap >= 1e-4)
+    assert int(tied.sum()) >= 5, "no tie at the k-th place: the case does not test the rule"
+    assert np.array_equal(ids.cpu().numpy()[use], ids_ref[use])
+    assert np.abs(w.cpu().numpy().astype(np.float64)[use] - w_ref[use]).max() <= W_TOL
+    _say(f"ties at the k-th place: {int(tied.sum())} of {T} tokens; compared {int(use.sum())}")
+
+
 @pytest.mark.parametrize("T,H,F,E,k", [
     (256, 128, 64, 16, 4),    # register-staged grouped FFN, fp32 y_perm
     (600, 256, 256, 4, 2),    # direct-to-LDS large tiles, k-blocked h, block-scaled fp16 y_perm
