@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kCapThreads) void cap_round_kernel(const float* __r
             kept[q] = false;
             p[q] = 0.0f;
         }
-        radix_select<Q>(key, k, sel);
+        radix_select<Q, true>(key, k, sel);
         write_slots<Q>(sel, kept, p, t, k, ids, nullptr);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(64) void cap_serial_kernel(const float* __restrict_
         bool sel[Q], kept[Q];
         float p[Q];
         token_keys<Q>(logits + t * ld, E, t, until, v, key);
-        radix_select<Q>(key, k, sel);
+        radix_select<Q, true>(key, k, sel);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             kept[q] = sel[q];

@@ -31,7 +31,7 @@ constexpr int kQMax = 16;              // experts per lane: E <= 1024
 // Top-k of one token whose E logits sit in LDS at lg[0..E) (E <= 64*Q), one
 // whole wave: radix select, softmax over the selection (+ drop), slots in
 // ascending expert id (topk.hpp).
-template <int Q>
+template <int Q, bool EARLY = false>
 __device__ void topk_select(const float* lg, int E, int k, float drop, long t, int32_t* __restrict__ ids,
                             float* __restrict__ wout) {
     const int l = lane_id();
@@ -45,7 +45,7 @@ __device__ void topk_select(const float* lg, int E, int k, float drop, long t, i
     }
     bool sel[Q], kept[Q];
     float p[Q];
-    radix_select<Q>(key, k, sel);
+    radix_select<Q, EARLY>(key, k, sel);
     softmax_drop<Q>(v, sel, drop, p, kept);
     write_slots<Q>(sel, kept, p, t, k, ids, wout);
 }
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void route_reduce_block_kernel(const float* __
         for (int rr = 0; rr < R; ++rr) sum += part[rr][j];
         lg[j] = sum + (bias != nullptr ? bias[j] : 0.0f);
     }
-    topk_select<(EP + kWave - 1) / kWave>(lg, E, k, drop, t, ids, wout);
+    topk_select<(EP + kWave - 1) / kWave, true>(lg, E, k, drop, t, ids, wout);  // few tokens: early exit pays
 }
 
 // Splits of the H loop: the smallest power of two that gives >= 512

@@ -31,11 +31,17 @@ __device__ __forceinline__ float wave_max(float v) {
 // The k largest keys of the wave, ties to the lower expert id:
 //  1. radix select: the k-th largest key tau is built bit by bit from the
 //     top, keeping a bit when at least k keys are >= the candidate (a wave
-//     ballot and a popcount per slice; no cross-lane shuffles);
+//     ballot and a popcount per slice; no cross-lane shuffles). With EARLY,
+//     a candidate with exactly k keys >= it ends the walk: those keys are
+//     the k largest and no tie can straddle the k-th place;
 //  2. keys > tau are selected; keys == tau fill the remaining places in
 //     ascending expert id.
+// EARLY pays two scalar instructions per bit for the shorter walk: it helps
+// where few waves run the select (capacity rounds on the skewed workload:
+// 173 -> 150 us) and costs where many do, since the walk is scalar-bound
+// there (prefill reduction 7.4 -> 8.2 us).
 // Needs at least k keys > 0.
-template <int Q>
+template <int Q, bool EARLY = false>
 __device__ __forceinline__ void radix_select(const uint32_t (&key)[Q], int k, bool (&sel)[Q]) {
     const int l = lane_id();
     uint32_t tau = 0;
@@ -44,6 +50,11 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[Q], int k, bo
         int c = 0;
 #pragma unroll
         for (int q = 0; q < Q; ++q) c += __popcll(__ballot(key[q] >= cand));
+        if (EARLY && c == k) {  // wave-uniform (ballot counts)
+#pragma unroll
+            for (int q = 0; q < Q; ++q) sel[q] = key[q] >= cand;
+            return;
+        }
         if (c >= k) tau = cand;
     }
     int n_gt = 0;
