@@ -260,6 +260,8 @@ def test_permute_oracle_fed(dev, T, E):
     (512, 16, 4),      # H loop split across workgroups, top-k in the reduction kernel
     (16384, 16, 4),    # enough token blocks: no split, top-k fused into the router kernel
     (512, 256, 8),     # four logits per lane
+    (8192, 128, 8),    # 64 tokens per workgroup sharing each Wr stage, split H loop
+    (16384, 64, 4),    # 64 tokens per workgroup, top-k fused into the router kernel
 ])
 def test_router_exact_ties(dev, T, E, k):
     """Experts with identical router columns get bit-identical logits on both sides (each logit is the same

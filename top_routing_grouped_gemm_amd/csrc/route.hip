@@ -227,33 +227,38 @@ constexpr int kR2Rows = 32;
 constexpr int kR2BK = 64;
 constexpr int kR2Stages = 3;
 
-template <int EP>
+// RG row groups of 32 tokens share each Wr stage (4 waves per group): with
+// RG = 2 a workgroup reads each Wr slice once for 64 tokens, halving the Wr
+// traffic from L2, which dominates the router's loads at large T.
+template <int EP, int RG = 1>
 struct R2 {
-    static constexpr int A_BYTES = kR2Rows * kR2BK * 2;      // 4 KiB: one chunk per wave
+    static constexpr int NWV = 4 * RG, ROWS = kR2Rows * RG;  // waves, tokens per workgroup
+    static constexpr int A_BYTES = ROWS * kR2BK * 2;          // 4 KiB per group: one chunk per wave
     static constexpr int B_BYTES = kR2BK * EP * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int B_CHUNKS = B_BYTES / 4096;          // per wave
+    static constexpr int B_CHUNKS = B_BYTES / (1024 * NWV);  // per wave
     static constexpr int LOADS = 1 + B_CHUNKS;
     static constexpr int B_RCH = EP / 8;                     // 16-byte chunks per Wr row
     static constexpr int B_RPK = 1024 / (EP * 2);            // Wr rows per KiB
     static constexpr int NT = EP / 16;                       // 16-column MFMA tiles
     static constexpr int NTW = (NT + 3) / 4;                 // tiles per wave
-    static constexpr int LDS = (kR2Stages * STAGE > kR2Rows * EP * 4) ? kR2Stages * STAGE : kR2Rows * EP * 4;
-    static_assert(B_BYTES % 4096 == 0, "Wr tile must be whole 4 KiB chunks");
+    static constexpr int LDS = (kR2Stages * STAGE > ROWS * EP * 4) ? kR2Stages * STAGE : ROWS * EP * 4;
+    static_assert(B_BYTES % (1024 * NWV) == 0 && B_CHUNKS >= 1, "Wr tile must be whole KiB chunks per wave");
     __device__ static int swz_b(int r, int c) { return EP >= 128 ? dma::swz_b(r, c) : c; }
 };
 
-template <int EP, bool SPLIT>
-__global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr,
+template <int EP, bool SPLIT, int RG = 1>
+__global__ __launch_bounds__(256 * RG) void route_v2_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr,
                                                        const float* __restrict__ bias, int T, int H, int E, int k,
                                                        float drop, int steps_per_split, int32_t* __restrict__ ids,
                                                        float* __restrict__ wout, float* __restrict__ partial) {
-    using C = R2<EP>;
+    using C = R2<EP, RG>;
     __shared__ __align__(1024) uint8_t smem[C::LDS];
-    const int t0 = blockIdx.x * kR2Rows;
+    const int t0 = blockIdx.x * C::ROWS;
     const int sp = blockIdx.y;
     const int wave = threadIdx.x / kWave, l = lane_id();
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int rg = uwave / 4, wq = wave % 4;  // this wave's row group and its place in the group
     const int kbase = sp * steps_per_split * kR2BK;
 
     // global sources of this lane's LDS chunks
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restric
     const uint16_t* b_src[C::B_CHUNKS];
 #pragma unroll
     for (int i = 0; i < C::B_CHUNKS; ++i) {
-        const int c = uwave + 4 * i;
+        const int c = uwave + C::NWV * i;
         const int row = c * C::B_RPK + l / C::B_RCH;
         const int col = min(C::swz_b(row, l % C::B_RCH) * 8, E - 8);
         b_src[i] = Wr + (long)(kbase + row) * E + col;
@@ -272,7 +277,8 @@ __global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restric
         const uint32_t b0 = (uint32_t)(uintptr_t)(ring + stage * C::STAGE) + uwave * 1024;
         dma::lds_dma16(a_src + k0, b0);
 #pragma unroll
-        for (int i = 0; i < C::B_CHUNKS; ++i) dma::lds_dma16(b_src[i] + (long)k0 * E, b0 + C::A_BYTES + i * 4096);
+        for (int i = 0; i < C::B_CHUNKS; ++i)
+            dma::lds_dma16(b_src[i] + (long)k0 * E, b0 + C::A_BYTES + i * 1024 * C::NWV);
     };
 
     f32x4 acc[2][C::NTW];
@@ -288,12 +294,12 @@ __global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restric
             bf16x8 af[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int row = i * 16 + (l & 15);
+                const int row = rg * 32 + i * 16 + (l & 15);
                 af[i] = *(dma::lds_bf16x8*)(As + row * (kR2BK * 2) + dma::swz_a(row, (kk >> 3) + (l >> 4)) * 16);
             }
 #pragma unroll
             for (int j = 0; j < C::NTW; ++j) {
-                const int nt = wave + 4 * j;
+                const int nt = wq + 4 * j;
                 if (nt < C::NT) {
                     const int n = nt * 16 + 4 * (l & 3);
                     const int c = n >> 3, half = (n >> 2) & 1;
@@ -331,14 +337,14 @@ __global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restric
         // partial[sp][t][e], e over all EP columns (columns >= E are ignored later)
 #pragma unroll
         for (int j = 0; j < C::NTW; ++j) {
-            const int nt = wave + 4 * j;
+            const int nt = wq + 4 * j;
             if (nt < C::NT) {
                 const int e = nt * 16 + (l & 15);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int t = t0 + i * 16 + (l >> 4) * 4 + q;
+                        const int t = t0 + rg * 32 + i * 16 + (l >> 4) * 4 + q;
                         if (t < T) partial[((long)sp * T + t) * EP + e] = acc[i][j][q];
                     }
             }
@@ -350,18 +356,18 @@ __global__ __launch_bounds__(256) void route_v2_kernel(const uint16_t* __restric
     float* lg = (float*)smem;
 #pragma unroll
     for (int j = 0; j < C::NTW; ++j) {
-        const int nt = wave + 4 * j;
+        const int nt = wq + 4 * j;
         if (nt < C::NT) {
             const int e = nt * 16 + (l & 15);
             const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) lg[(i * 16 + (l >> 4) * 4 + q) * EP + e] = acc[i][j][q] + b;
+                for (int q = 0; q < 4; ++q) lg[(rg * 32 + i * 16 + (l >> 4) * 4 + q) * EP + e] = acc[i][j][q] + b;
         }
     }
     __syncthreads();
-    for (int m = wave; m < kR2Rows; m += 4) {
+    for (int m = wave; m < C::ROWS; m += C::NWV) {
         const long t = t0 + m;
         if (t < T) topk_select<(EP + kWave - 1) / kWave>(lg + m * EP, E, k, drop, t, ids, wout);
     }
@@ -472,16 +478,29 @@ inline int route_ep(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128
 template <int EP>
 hipError_t launch_v2(const uint16_t* x, const uint16_t* Wr, const float* bias, int T, int H, int E, int k, float drop,
                      int32_t* ids, float* w, float* partial, hipStream_t s) {
-    const int S = route_splits(T, H);
+    const int S = route_splits(T, H);  // the split the workspace is sized for
     const int steps = H / kR2BK / S;
-    const dim3 grid((T + kR2Rows - 1) / kR2Rows, S);
+    // many tokens: 64 per workgroup (two row groups on one Wr stage, 8 waves), so the same number of waves
+    // reads half as much of Wr from L2
+    constexpr int RG2 = EP >= 64 ? 2 : 1;  // a Wr stage splits into whole KiB chunks over 8 waves from EP = 64
+    const bool pair = RG2 == 2 && T >= 4096;
+    const int rows = pair ? 2 * kR2Rows : kR2Rows;
+    const dim3 grid((T + rows - 1) / rows, S);
     if (S == 1) {
-        hipLaunchKernelGGL((route_v2_kernel<EP, false>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, k, drop, steps,
-                           ids, w, (float*)nullptr);
+        if (pair)
+            hipLaunchKernelGGL((route_v2_kernel<EP, false, RG2>), grid, dim3(256 * RG2), 0, s, x, Wr, bias, T, H, E, k,
+                               drop, steps, ids, w, (float*)nullptr);
+        else
+            hipLaunchKernelGGL((route_v2_kernel<EP, false>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, k, drop,
+                               steps, ids, w, (float*)nullptr);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((route_v2_kernel<EP, true>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, k, drop, steps, ids,
-                       w, partial);
+    if (pair)
+        hipLaunchKernelGGL((route_v2_kernel<EP, true, RG2>), grid, dim3(256 * RG2), 0, s, x, Wr, bias, T, H, E, k, drop,
+                           steps, ids, w, partial);
+    else
+        hipLaunchKernelGGL((route_v2_kernel<EP, true>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, k, drop, steps,
+                           ids, w, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (S >= 16)
