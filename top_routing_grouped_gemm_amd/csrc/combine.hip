@@ -158,12 +158,12 @@ __global__ __launch_bounds__(256) void combine_f16s_kernel(const u32x4* __restri
 }
 
 template <bool PACKED>
-hipError_t combine(const void* y_perm, long lo_off, const int32_t* inv, const float* w, const float* y_shared, int T,
+hipError_t combine(const void* y_perm, long sc_off, const int32_t* inv, const float* w, const float* y_shared, int T,
                    int H, int k, Dtype out_dt, void* y, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if constexpr (PACKED) {
         const u32x4* vals = (const u32x4*)y_perm;
-        const int8_t* sc = (const int8_t*)((const uint8_t*)y_perm + lo_off);
+        const int8_t* sc = (const int8_t*)((const uint8_t*)y_perm + sc_off);  // the scale bytes after the fp16 values
         if (out_dt == kBF16)
             hipLaunchKernelGGL((combine_f16s_kernel<true>), dim3(T), dim3(256), 0, s, vals, sc, inv, w,
                                (const float4*)y_shared, H / 8, k, y);
