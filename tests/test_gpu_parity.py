@@ -255,6 +255,39 @@ def test_permute_oracle_fed(dev, T, E):
     check_routing(g, r, dref, I.x)
 
 
+# ------------------------------------------- block-scaled fp16 extremes --
+def test_scaled16_dynamic_range(dev):
+    """The one-call layer's block-scaled fp16 y_perm at the ends of its range. W2 columns are scaled so that
+    y_perm has, per 32-column block: one column 1e-12 below the rest (it falls under fp16's normal range after
+    scaling), a block near 1e-36 (its exponent clamps at -127), a block near 1e20, an all-zero block (s = 0),
+    and ordinary blocks. The one-call result must stay within the element-wise rounding bound of the step-wise
+    (fp32 y_perm) result. The step-wise result meets the usual bar of the oracle on each block at its own scale
+    (the ordinary columns, and the 1e20 block alone); the 1e-36 block is left out of that comparison, since most
+    of its bf16 weights are subnormal, which the matrix cores may flush to zero."""
+    I = gen.make_inputs("tiny", T=600, H=256, F=256, E=4, k=2, dtype="bf16", seed=151)  # 256-row tiles, packed W2
+    d = gen.to_device(I, dev)
+    colscale = torch.ones(I.H, dtype=torch.float32)
+    colscale[5] = 1e-12
+    colscale[32:64] = 1e-36
+    colscale[64:96] = 1e20
+    colscale[96:128] = 0.0
+    d["W2"] = (d["W2"].float() * colscale.to(dev)).to(torch.bfloat16)
+    g = run_steps(d, I, dev)
+    A = int(g["off"][-1].item())
+    y1 = moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], I.k, I.drop)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y1).all())
+    assert bool((y1[:, 96:128] == 0).all())
+    bound = scaled16_bound(g["y_perm"], A, g["inv"], g["w"], g["y"])
+    assert bool(((y1 - g["y"]).abs().double() <= bound).all()), "one-call y outside the fp16 rounding bound"
+    W2 = d["W2"].float().double().cpu().numpy()
+    ref = oracle.forward(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.f64(I.W1()), W2, I.k, I.drop)
+    check_routing(g, ref.route, ref.dispatch)
+    y = g["y"].double().cpu().numpy()
+    for cols in (np.r_[0:32, 128:256], np.r_[64:96]):
+        check_y(y[:, cols], ref.y[:, cols])
+
+
 # ---------------------------------------------------------- exact ties --
 @pytest.mark.parametrize("T,E,k", [
     (512, 16, 4),      # H loop split across workgroups, top-k in the reduction kernel
