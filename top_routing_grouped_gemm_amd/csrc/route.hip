@@ -551,9 +551,16 @@ hipError_t launch_logits(const uint16_t* x, const uint16_t* Wr, const float* bia
                          float* logits, float* partial, hipStream_t s) {
     const int S = route_splits(T, H);
     const int steps = H / kR2BK / S;
-    const dim3 grid((T + kR2Rows - 1) / kR2Rows, S);
-    hipLaunchKernelGGL((route_v2_kernel<EP, true>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, 1, 0.0f, steps,
-                       (int32_t*)nullptr, (float*)nullptr, partial);
+    constexpr int RG2 = EP >= 64 ? 2 : 1;  // as launch_v2: 64 tokens per workgroup at large T
+    const bool pair = RG2 == 2 && T >= 4096;
+    const int rows = pair ? 2 * kR2Rows : kR2Rows;
+    const dim3 grid((T + rows - 1) / rows, S);
+    if (pair)
+        hipLaunchKernelGGL((route_v2_kernel<EP, true, RG2>), grid, dim3(256 * RG2), 0, s, x, Wr, bias, T, H, E, 1,
+                           0.0f, steps, (int32_t*)nullptr, (float*)nullptr, partial);
+    else
+        hipLaunchKernelGGL((route_v2_kernel<EP, true>), grid, dim3(256), 0, s, x, Wr, bias, T, H, E, 1, 0.0f, steps,
+                           (int32_t*)nullptr, (float*)nullptr, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long n = (long)T * EP;
