@@ -28,18 +28,40 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def event_time_ms(fn, reps, stream):
+def event_time_ms(fn, reps, stream, evict=None):
+    """Mean HIP-event time of fn on `stream` over `reps` calls after one untimed call. With `evict` (a device
+    buffer larger than the 256 MB MALL), every rep is timed on its own after a write of that whole buffer, so the
+    rep starts with its inputs out of the last-level cache; without it the reps run back to back."""
     import torch
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     fn()
-    start.record(stream)
-    for _ in range(reps):
+    if evict is None:
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+        end.synchronize()
+        return start.elapsed_time(end) / reps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for r in range(reps):
+        evict.fill_(r & 0x7F)  # same stream as fn: the write completes before the rep starts
+        starts[r].record(stream)
         fn()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / reps
+        ends[r].record(stream)
+    ends[-1].synchronize()
+    return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / reps
+
+
+EVICT_BYTES = 1 << 30  # > 4x the 256 MB MALL
+
+
+def evict_buffer():
+    import torch
+
+    return torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
 
 
 def stage_times(d, I, reps):
@@ -81,22 +103,30 @@ def stage_times(d, I, reps):
     torch.cuda.synchronize()
     A = int(off[-1].item())
     counts = (off[1:] - off[:-1]).cpu()
-    out = {name: event_time_ms(fn, reps, s) for name, fn in
-           (("route", route), ("permute", permute), ("grouped_ffn", ffn), ("combine", combine))}
-    return out, A, counts
+    stages = (("route", route), ("permute", permute), ("grouped_ffn", ffn), ("combine", combine))
+    out = {name: event_time_ms(fn, reps, s) for name, fn in stages}
+    ev = evict_buffer()
+    cold = {name: event_time_ms(fn, reps, s, evict=ev) for name, fn in stages}
+    del ev
+    return out, cold, A, counts
 
 
-def bytes_model(I, A, experts_hit):
-    """Algorithmic HBM bytes per call of each stage (each array read or written once)."""
+def bytes_model(I, A, experts_hit, out_bytes=4):
+    """Algorithmic HBM bytes per call of each stage (each array read or written once).
+
+    out_bytes = 4: the formats the step-wise calls actually use (fp32 y_perm, y_shared and y); out_bytes = b
+    (the operand width, 2 for bf16): the method's own formats, y_perm and y in the operand type, the byte
+    counts of the hot-path scope table. h never leaves the grouped FFN and is not counted."""
     b = I.elem_bytes
+    o = out_bytes
     T, H, F, E, k = I.T, I.H, I.F, I.E, I.k
     Fs = I.Fs
-    shared_ffn = (2 * H * Fs * b + T * H * b + T * H * 4) if Fs else 0  # W1s, W2s, x read, y_shared written
+    shared_ffn = (2 * H * Fs * b + T * H * b + T * H * o) if Fs else 0  # W1s, W2s, x read, y_shared written
     return {
         "route": T * H * b + H * E * b + T * k * 8,
         "permute": T * H * b + A * H * b + T * k * 8 * 2 + A * 4,
-        "grouped_ffn": experts_hit * 2 * H * F * b + A * H * b + A * H * 4 + shared_ffn,
-        "combine": A * H * 4 + T * k * 8 + T * H * 4 + (T * H * 4 if Fs else 0),
+        "grouped_ffn": experts_hit * 2 * H * F * b + A * H * b + A * H * o + shared_ffn,
+        "combine": A * H * o + T * k * 8 + T * H * o + (T * H * o if Fs else 0),
     }
 
 
@@ -161,10 +191,15 @@ def run_workload(name, steps, warmup, stage_reps, graph=False):
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t) * 1e3 / steps
         del g
-    st, A, counts = stage_times(d, I, stage_reps)
+    st, cold, A, counts = stage_times(d, I, stage_reps)
     hit = int((counts > 0).sum())
     flops = 4.0 * A * I.H * I.F + 4.0 * I.T * I.H * I.Fs  # routed experts + shared expert
     byts = bytes_model(I, A, hit)
+    byts_m = bytes_model(I, A, hit, out_bytes=I.elem_bytes)
+
+    def frac(bm, times):
+        return {k_: round(bm[k_] / (times[k_] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k_ in times}
+
     res = {
         "T": I.T, "H": I.H, "F": I.F, "E": I.E, "k": I.k, "A": A, "experts_hit": hit,
         "rows_per_expert": {"min": int(counts.min()), "max": int(counts.max()),
@@ -172,14 +207,22 @@ def run_workload(name, steps, warmup, stage_reps, graph=False):
         "ms_per_step": ms, "tokens_per_s": I.T / (ms * 1e-3),
         **({"graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": I.T / (graph_ms * 1e-3)}} if graph_ms else {}),
         "stages_ms": {k: round(v, 5) for k, v in st.items()},
+        "stages_ms_mall_evicted": {k: round(v, 5) for k, v in cold.items()},
         "stage_gbs": {k: round(byts[k] / (st[k] * 1e-3) / 1e9, 1) for k in st},
-        "stage_hbm_frac": {k: round(byts[k] / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k in st},
+        "stage_hbm_frac": frac(byts, st),
+        "stage_hbm_frac_mall_evicted": frac(byts, cold),
+        "stage_hbm_frac_method_bytes": frac(byts_m, st),
+        "stage_hbm_frac_method_bytes_mall_evicted": frac(byts_m, cold),
         "grouped_ffn_tflops": flops / (st["grouped_ffn"] * 1e-3) / 1e12,
         "grouped_ffn_mfma_frac": round(flops / (st["grouped_ffn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "weight_stream_gbs": round((hit * 2 * I.H * I.F + 2 * I.H * I.Fs) * I.elem_bytes
                                    / (st["grouped_ffn"] * 1e-3) / 1e9, 1),
         "grouped_ffn_flops": flops,
         "algorithmic_bytes": byts,
+        "method_bytes": byts_m,
+        "bytes_note": "algorithmic_bytes: each array once in the formats the step-wise calls use (fp32 y_perm, "
+                      "y_shared, y); method_bytes: y_perm, y_shared and y in the operand type (the scope table's "
+                      "counts); *_mall_evicted: each rep timed alone after a 1 GiB write that evicts the MALL",
     }
     del d, ws
     torch.cuda.empty_cache()
@@ -429,6 +472,55 @@ def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
             "stages_s": {k_: round(v / reps, 3) for k_, v in stage.items()}}
 
 
+def calibration():
+    """Practical ceilings on this machine, measured with the library's calibration kernels: the bare bf16 MFMA loop
+    with one and two waves per SIMD (256 workgroups of 4 / 8 waves), and a streaming read of 2 GiB."""
+    import torch
+
+    import top_routing_grouped_gemm_amd as moe
+
+    s = torch.cuda.current_stream()
+    out = {}
+    for waves in (4, 8):
+        iters = 4096
+        sink = torch.empty(256 * waves * 64, dtype=torch.float32, device="cuda")
+        flops = moe.moe_calibrate_mfma_bf16(256, waves, iters, sink)
+        ms = event_time_ms(lambda: moe.moe_calibrate_mfma_bf16(256, waves, iters, sink), 5, s)
+        out[f"mfma_32x32x16_bf16_{waves // 4}_wave_per_simd_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    for wg in (1024, 4096):
+        sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+        nbytes = moe.moe_calibrate_stream_read(buf, wg, sink)
+        ms = event_time_ms(lambda: moe.moe_calibrate_stream_read(buf, wg, sink), 5, s)
+        out[f"stream_read_{wg}_workgroups_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf
+    out["note"] = "bare-loop and streaming-read ceilings (library calibration kernels); context for the fractions"
+    return out
+
+
+def ffn_only(name, reps):
+    """Only the step-wise grouped FFN of one workload, `reps` times (for counter passes: one kernel pair per
+    call and nothing else from the library in between)."""
+    import torch
+
+    import gen
+    import top_routing_grouped_gemm_amd as moe
+
+    dev = torch.device("cuda:0")
+    I = gen.make_inputs(name)
+    d = gen.to_device(I, dev)
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], I.k, I.drop)
+    x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, I.E)
+    y_perm = torch.empty((I.T * I.k, I.H), dtype=torch.float32, device=dev)
+    fws = torch.empty(moe.moe_ffn_workspace_bytes(I.T, I.F, I.E, I.k, 0, d["x"].dtype), dtype=torch.uint8,
+                      device=dev)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], I.T, I.k, y_perm=y_perm, ws=fws)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": name, "ffn_calls": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +531,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["tiny", "decode", "prefill", "mixtral_shared", "skew"], default=None,
                     help="time one workload only (profiling runs and the per-workload table); prints its stage times")
+    ap.add_argument("--ffn-only", type=int, default=0,
+                    help="with --only: run only the step-wise grouped FFN this many times (counter passes)")
+    ap.add_argument("--calibrate", action="store_true", help="print only the MFMA and streaming-read ceilings")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
@@ -470,6 +565,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return
+    if args.calibrate:
+        print(json.dumps(calibration()), flush=True)
+        return
+    if args.only and args.ffn_only:
+        ffn_only(args.only, args.ffn_only)
         return
     if args.only and args.padded:
         print(json.dumps(padded_times(args.only)), flush=True)
@@ -534,6 +635,20 @@ def main():
                                                              "weight_bytes", "weight_stream_gbs")}
         mx = mx_times("decode", max(args.steps, 50), max(args.stage_reps, 100))
         line["decode_mxfp8_experts"] = {k_: mx[k_] for k_ in ("forward_ms", "tokens_per_s", "grouped_ffn_ms")}
+    # the other full-size workloads: the Mixtral-like layer with its shared expert (MFMA-bound) and the skewed
+    # layer (weight-stream bound)
+    for name in ("mixtral_shared", "skew"):
+        Iw, r = run_workload(name, max(5, args.steps // 4), 2, max(5, args.stage_reps // 2))
+        wbytes = (r["experts_hit"] * 2 * Iw.H * Iw.F + 2 * Iw.H * Iw.Fs) * Iw.elem_bytes
+        keep = ("T", "H", "F", "E", "k", "A", "experts_hit", "rows_per_expert", "ms_per_step", "tokens_per_s",
+                "stages_ms", "stages_ms_mall_evicted", "stage_hbm_frac", "stage_hbm_frac_method_bytes",
+                "grouped_ffn_tflops", "grouped_ffn_mfma_frac")
+        line[name] = {k_: r[k_] for k_ in keep}
+        line[name]["weight_stream_gbs"] = round(wbytes / (r["stages_ms"]["grouped_ffn"] * 1e-3) / 1e9, 1)
+        line[name]["weight_stream_hbm_frac"] = round(line[name]["weight_stream_gbs"] / PEAK_HBM_GBS, 4)
+        if Iw.Fs:
+            line[name]["Fs"] = Iw.Fs
+    line["calibration"] = calibration()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle) ...")
         line["cpu_baseline"] = cpu_baseline("prefill")

@@ -76,7 +76,8 @@ def build(force: bool = True) -> str:
 
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+        # separate libm sin and cos calls (no merged sincos): the deviates keep the same bits as every earlier build
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-fno-builtin-sin", "-fno-builtin-cos",
                os.path.join(_HERE, "philox_normal.c"), "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
@@ -328,8 +329,11 @@ def storage_to_torch(a: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
 
 
-def to_device(I: MoEInputs, device="cuda", experts_per_chunk: Optional[int] = None) -> dict:
-    """Copy every array of a workload to `device`; expert weights are drawn and copied in chunks."""
+def to_device(I: MoEInputs, device="cuda", experts_per_chunk: Optional[int] = None, keep_host: bool = False) -> dict:
+    """Copy every array of a workload to `device`; expert weights are drawn and copied in chunks.
+
+    keep_host: also return the drawn expert weights in storage precision as ``W1_host`` [E,H,F] and
+    ``W2_host`` [E,F,H] (numpy), so that a caller needing them on the host does not draw them again."""
     import torch
 
     tdt = torch.bfloat16 if I.dtype == "bf16" else torch.float32
@@ -340,11 +344,19 @@ def to_device(I: MoEInputs, device="cuda", experts_per_chunk: Optional[int] = No
         experts_per_chunk = max(1, (256 << 20) // max(1, per_expert))
     W1 = torch.empty((I.E, I.H, I.F), dtype=tdt, device=device)
     W2 = torch.empty((I.E, I.F, I.H), dtype=tdt, device=device)
+    host = {"W1": [], "W2": []}
     for e0 in range(0, I.E, experts_per_chunk):
         e1 = min(I.E, e0 + experts_per_chunk)
-        W1[e0:e1].copy_(storage_to_torch(I.W1(e0, e1), I.dtype))
-        W2[e0:e1].copy_(storage_to_torch(I.W2(e0, e1), I.dtype))
+        w1, w2 = I.W1(e0, e1), I.W2(e0, e1)
+        W1[e0:e1].copy_(storage_to_torch(w1, I.dtype))
+        W2[e0:e1].copy_(storage_to_torch(w2, I.dtype))
+        if keep_host:
+            host["W1"].append(w1)
+            host["W2"].append(w2)
     out["W1"], out["W2"] = W1, W2
+    if keep_host:
+        out["W1_host"] = np.concatenate(host["W1"])
+        out["W2_host"] = np.concatenate(host["W2"])
     out["W1s"] = storage_to_torch(I.W1s(), I.dtype).to(device) if I.Fs else None
     out["W2s"] = storage_to_torch(I.W2s(), I.dtype).to(device) if I.Fs else None
     return out

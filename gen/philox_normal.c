@@ -57,18 +57,6 @@ static inline double unit53(uint32_t hi, uint32_t lo) {
     return ((double)v + 0.5) * (1.0 / 9007199254740992.0);
 }
 
-static inline double normal_at(uint32_t seed, uint32_t tensor_id, uint32_t attempt, uint64_t i) {
-    uint64_t blk = i >> 1;
-    uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), attempt, 0u};
-    uint32_t key[2] = {seed, tensor_id};
-    uint32_t r[4];
-    moegen_philox4x32_10(ctr, key, r);
-    double u1 = unit53(r[0], r[1]);
-    double u2 = unit53(r[2], r[3]);
-    double rad = sqrt(-2.0 * log(u1));
-    double th = 6.283185307179586476925286766559 * u2;
-    return (i & 1) ? rad * sin(th) : rad * cos(th);
-}
 
 /* fp32 -> bf16 bits, round to nearest even (inputs are finite). */
 static inline uint16_t f32_to_bf16_rne(float f) {
@@ -79,28 +67,59 @@ static inline uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+/* Both deviates of Philox block `blk`: element 2*blk is rad*cos(th), element 2*blk+1 is rad*sin(th)
+   (Box-Muller on the block's two 53-bit uniforms); one Philox evaluation serves both. */
+static inline void normal_pair(uint32_t seed, uint32_t tensor_id, uint32_t attempt, uint64_t blk, double* d0,
+                               double* d1) {
+    uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), attempt, 0u};
+    uint32_t key[2] = {seed, tensor_id};
+    uint32_t r[4];
+    moegen_philox4x32_10(ctr, key, r);
+    double u1 = unit53(r[0], r[1]);
+    double u2 = unit53(r[2], r[3]);
+    double rad = sqrt(-2.0 * log(u1));
+    double th = 6.283185307179586476925286766559 * u2;
+    *d0 = rad * cos(th);
+    *d1 = rad * sin(th);
+}
+
+/* Elements [i0, i0+n) of a stream through a per-element store callback, one Philox block per pair. */
+#define MOEGEN_FILL(STORE)                                                                     \
+    do {                                                                                       \
+        uint64_t b0 = i0 >> 1, b1 = (i0 + n + 1) >> 1;                                        \
+        _Pragma("omp parallel for schedule(static)")                                           \
+        for (int64_t b = (int64_t)b0; b < (int64_t)b1; ++b) {                                  \
+            double v[2];                                                                       \
+            normal_pair(seed, tensor_id, attempt, (uint64_t)b, &v[0], &v[1]);                  \
+            for (int h = 0; h < 2; ++h) {                                                      \
+                uint64_t i = 2 * (uint64_t)b + (uint64_t)h;                                    \
+                if (i >= i0 && i < i0 + n) { STORE(i - i0, v[h] * std); }                      \
+            }                                                                                  \
+        }                                                                                      \
+    } while (0)
+
 /* Unrounded deviates (scaled by std), elements [i0, i0+n). */
 void moegen_normal_f64(uint32_t seed, uint32_t tensor_id, uint32_t attempt, uint64_t i0,
                        uint64_t n, double std, double* out) {
-    #pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < (int64_t)n; ++j)
-        out[j] = normal_at(seed, tensor_id, attempt, i0 + (uint64_t)j) * std;
+#define ST_F64(j, v) out[j] = (v)
+    MOEGEN_FILL(ST_F64);
+#undef ST_F64
 }
 
 /* Deviates rounded to fp32. */
 void moegen_normal_f32(uint32_t seed, uint32_t tensor_id, uint32_t attempt, uint64_t i0,
                        uint64_t n, double std, float* out) {
-    #pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < (int64_t)n; ++j)
-        out[j] = (float)(normal_at(seed, tensor_id, attempt, i0 + (uint64_t)j) * std);
+#define ST_F32(j, v) out[j] = (float)(v)
+    MOEGEN_FILL(ST_F32);
+#undef ST_F32
 }
 
 /* Deviates rounded to fp32, then to bf16; written as raw bf16 bit patterns. */
 void moegen_normal_bf16(uint32_t seed, uint32_t tensor_id, uint32_t attempt, uint64_t i0,
                         uint64_t n, double std, uint16_t* out) {
-    #pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < (int64_t)n; ++j)
-        out[j] = f32_to_bf16_rne((float)(normal_at(seed, tensor_id, attempt, i0 + (uint64_t)j) * std));
+#define ST_BF16(j, v) out[j] = f32_to_bf16_rne((float)(v))
+    MOEGEN_FILL(ST_BF16);
+#undef ST_BF16
 }
 
 /* Raw Philox words for a block range, for known-answer checks. */

@@ -387,6 +387,25 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* inv, void* ws,
                       size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Measurement aids (not steps of the layer): the practical ceilings against
+ * which the layer's kernels are read.
+ *
+ * moe_calibrate_mfma_bf16: `workgroups` workgroups of `waves_per_workgroup`
+ *   (1..8) waves; each wave issues iters x 8 independent
+ *   v_mfma_f32_32x32x16_bf16 and nothing else, i.e.
+ *   workgroups * waves_per_workgroup * iters * 8 * 32768 FLOP. One float per
+ *   thread goes to sink[workgroups * waves_per_workgroup * 64] (keeps the
+ *   loop from being removed; the values mean nothing).
+ * moe_calibrate_stream_read: reads `bytes` (a multiple of 16) of `buf` once
+ *   with 16-byte loads from `workgroups` workgroups of 256 threads, one float
+ *   per thread to sink[workgroups * 256].
+ * Both return MOE_ERR_INVALID_ARG for sizes outside these ranges or a null
+ * pointer, MOE_ERR_HIP if the launch fails.
+ */
+int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, float* sink, hipStream_t stream);
+int moe_calibrate_stream_read(const void* buf, size_t bytes, int workgroups, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

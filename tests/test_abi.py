@@ -249,3 +249,78 @@ def test_mxfp8_rejects(lib):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(ImportError):
         moe.load_library(str(tmp_path / "missing.so"))
+
+
+# ------------------------------------------------ binding argument checks --
+def test_binding_rejects_mismatched_tensors(lib):
+    """The Python binding validates every tensor's dtype, shape and device against the sizes of the call before a
+    pointer reaches the library (a short or mistyped buffer would make a kernel read or write out of bounds).
+    CPU tensors get through these checks only when everything else is right; the last check refuses them."""
+    torch = pytest.importorskip("torch")
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    T, H, F, E, k = 8, 64, 32, 4, 2
+    x = torch.zeros((T, H), dtype=bf)
+    Wr = torch.zeros((H, E), dtype=bf)
+    W1 = torch.zeros((E, H, F), dtype=bf)
+    W2 = torch.zeros((E, F, H), dtype=bf)
+    ids = torch.zeros((T, k), dtype=i32)
+    w = torch.zeros((T, k), dtype=f32)
+
+    def raises(exc, match, fn, *a, **kw):
+        with pytest.raises(exc, match=match):
+            fn(*a, **kw)
+
+    # moe_forward: operand dtypes and shapes
+    raises(TypeError, "W1 has dtype", moe.moe_forward, x, Wr, None, W1.float(), W2, k)
+    raises(TypeError, "x has dtype", moe.moe_forward, x.half(), Wr, None, W1, W2, k)
+    raises(ValueError, "Wr has shape", moe.moe_forward, x, Wr[:32], None, W1, W2, k)
+    raises(ValueError, "W2 has shape", moe.moe_forward, x, Wr, None, W1, W2.transpose(1, 2).contiguous(), k)
+    raises(ValueError, "W1 has shape", moe.moe_forward, x, Wr, None, W1[:3], W2, k)
+    raises(ValueError, "bias has shape", moe.moe_forward, x, Wr, torch.zeros(E + 1), W1, W2, k)
+    raises(TypeError, "bias has dtype", moe.moe_forward, x, Wr, torch.zeros(E, dtype=torch.float64), W1, W2, k)
+    raises(ValueError, "y has shape", moe.moe_forward, x, Wr, None, W1, W2, k, y=torch.zeros((T - 1, H)))
+    raises(ValueError, "topk_ids has shape", moe.moe_forward, x, Wr, None, W1, W2, k, topk_ids=ids[:, :1].clone())
+    raises(TypeError, "inv has dtype", moe.moe_forward, x, Wr, None, W1, W2, k, inv=ids.long())
+    raises(ValueError, "expert_offsets has shape", moe.moe_forward, x, Wr, None, W1, W2, k,
+           expert_offsets=torch.zeros(E, dtype=i32))
+    raises(ValueError, "W2s has shape", moe.moe_forward, x, Wr, None, W1, W2, k, W1s=torch.zeros((H, 16), dtype=bf),
+           W2s=torch.zeros((8, H), dtype=bf))
+    raises(ValueError, "both W1s and W2s", moe.moe_forward, x, Wr, None, W1, W2, k,
+           W1s=torch.zeros((H, 16), dtype=bf))
+    raises(TypeError, "ws has dtype", moe.moe_forward, x, Wr, None, W1, W2, k, ws=torch.zeros(16, dtype=f32))
+    raises(ValueError, "must be on the GPU", moe.moe_forward, x, Wr, None, W1, W2, k)  # everything else is right
+
+    # moe_route / moe_permute / moe_grouped_ffn / moe_combine
+    raises(ValueError, "Wr has shape", moe.moe_route, x, torch.zeros((H + 8, E), dtype=bf), None, k)
+    raises(ValueError, "topk_w has shape", moe.moe_route, x, Wr, None, k, topk_w=torch.zeros((T, k + 1)))
+    raises(ValueError, "must be on the GPU", moe.moe_route, x, Wr, None, k)
+    raises(ValueError, "x_perm has shape", moe.moe_permute, x, ids, w, E, x_perm=torch.zeros((T * k - 1, H), dtype=bf))
+    raises(TypeError, "x_perm has dtype", moe.moe_permute, x, ids, w, E, x_perm=torch.zeros((T * k, H)))
+    raises(ValueError, "row_token has shape", moe.moe_permute, x, ids, w, E, row_token=torch.zeros(T, dtype=i32))
+    raises(TypeError, "topk_ids has dtype", moe.moe_permute, x, ids.long(), w, E)
+    x_perm = torch.zeros((T * k, H), dtype=bf)
+    off = torch.zeros(E + 1, dtype=i32)
+    raises(ValueError, "x_perm has shape", moe.moe_grouped_ffn, x_perm[:-1].contiguous(), off, W1, W2, T, k)
+    raises(ValueError, "expert_offsets has shape", moe.moe_grouped_ffn, x_perm, off[:-1].contiguous(), W1, W2, T, k)
+    raises(TypeError, "W2 has dtype", moe.moe_grouped_ffn, x_perm, off, W1, W2.float(), T, k)
+    raises(ValueError, "y_perm has shape", moe.moe_grouped_ffn, x_perm, off, W1, W2, T, k,
+           y_perm=torch.zeros((T * k, H - 8)))
+    raises(TypeError, "y_perm has dtype", moe.moe_grouped_ffn, x_perm, off, W1, W2, T, k,
+           y_perm=torch.zeros((T * k, H), dtype=bf))
+    raises(ValueError, "must be on the GPU", moe.moe_grouped_ffn, x_perm, off, W1, W2, T, k)
+    y_perm = torch.zeros((T * k, H))
+    raises(ValueError, "topk_w has shape", moe.moe_combine, y_perm, ids, w[:, :1].contiguous())
+    raises(ValueError, "y_shared has shape", moe.moe_combine, y_perm, ids, w, y_shared=torch.zeros((T, H + 8)))
+    raises(TypeError, "y has dtype", moe.moe_combine, y_perm, ids, w, y=torch.zeros((T, H), dtype=torch.float16))
+    raises(ValueError, "must be on the GPU", moe.moe_combine, y_perm, ids, w)
+
+    # quantised expert formats: codes and scales must have the sizes the quantisers write
+    W1q = torch.zeros(moe.moe_fp8_weight_bytes(E, H, F), dtype=torch.uint8)
+    W2q = torch.zeros(moe.moe_fp8_weight_bytes(E, F, H), dtype=torch.uint8)
+    s1, s2 = torch.zeros((E, F)), torch.zeros((E, H))
+    raises(ValueError, "W1q has shape", moe.moe_forward_fp8, x, Wr, None, W1q[:-1].contiguous(), s1, W2q, s2, k)
+    raises(ValueError, "W2_scale has shape", moe.moe_forward_fp8, x, Wr, None, W1q, s1, W2q, s2[:, :-1].contiguous(),
+           k)
+    raises(ValueError, "must be on the GPU", moe.moe_forward_fp8, x, Wr, None, W1q, s1, W2q, s2, k)
+    raises(ValueError, "Wq has shape", moe.moe_quantize_fp8, W1, Wq=W1q[:-1].contiguous())
+

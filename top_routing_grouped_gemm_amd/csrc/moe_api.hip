@@ -173,6 +173,58 @@ int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* off
     return MOE_OK;
 }
 
+// Device buffers of one forward pass inside the caller workspace.
+struct FwdBuffers {
+    int32_t *ids, *off, *inv, *row_token, *partial;
+    float *w, *y_perm, *y_sh;
+    void *x_perm, *ffn, *route;
+};
+
+int check_forward(const void* x, const void* Wr, const void* W1, const void* W2, const void* W1s, const void* W2s,
+                  int Fs, int T, int H, int F, int E, int k, float drop_thresh, moe_dtype_t dt, const void* y,
+                  moe_dtype_t out_dt) {
+    if (!valid_dtype(dt) || !valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
+    if (!x || !Wr || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
+    if ((W1s == nullptr) != (W2s == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (W1s != nullptr) {
+        if (Fs < 1) return MOE_ERR_INVALID_ARG;
+        if (Fs % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+// The launch sequence of moe_forward on the buffers in b (caller-given debug outputs replace their buffers).
+int enqueue_forward(const void* x, const void* Wr, const float* bias, const void* W1, const void* W2,
+                    const void* W1s, const void* W2s, int fs, int T, int H, int F, int E, int k, float drop_thresh,
+                    moe_dtype_t dt, void* y, moe_dtype_t out_dt, int32_t* topk_ids, float* topk_w,
+                    int32_t* expert_offsets, int32_t* inv, const FwdBuffers& b, hipStream_t stream) {
+    int32_t* ids = topk_ids ? topk_ids : b.ids;
+    float* w = topk_w ? topk_w : b.w;
+    int32_t* off = expert_offsets ? expert_offsets : b.off;
+    int32_t* iv = inv ? inv : b.inv;
+    // direct-to-LDS shapes: the W1 launch gathers x rows itself (x_perm is never written) and the W2 launch
+    // writes y_perm as block-scaled fp16 (the combine reads 2 + 1/32 bytes per value instead of 4)
+    const moe::TileCfg cfg = moe::choose_tile((long)T * k, E);
+    const bool gather = moe::ffn_up_gathers(cfg, H, F, (Dtype)dt);
+    const bool packed = moe::ffn_down_packs(cfg, F, H, (Dtype)dt);
+    int st;
+    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, b.route, stream));
+    if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, b.x_perm, off, b.row_token, iv, b.partial, !gather,
+                              stream)) != MOE_OK)
+        return st;
+    if ((st = enqueue_ffn(b.x_perm, gather ? b.row_token : nullptr, off, W1, W2, T, H, F, E, k, dt, b.y_perm, x, W1s,
+                          W2s, fs, b.y_sh, b.ffn, packed, stream)) != MOE_OK)
+        return st;
+    if (packed)
+        return hip_status(
+            moe::launch_combine_packed(b.y_perm, (long)T * k, iv, w, b.y_sh, T, H, k, (Dtype)out_dt, y, stream));
+    return hip_status(moe::launch_combine(b.y_perm, iv, w, b.y_sh, T, H, k, (Dtype)out_dt, y, stream));
+}
+
 int check_shared(const void* x, const void* W1s, const void* W2s, int Fs, const float* y_shared) {
     if (W1s == nullptr && W2s == nullptr) return MOE_OK;
     if (W1s == nullptr || W2s == nullptr || x == nullptr || y_shared == nullptr) return MOE_ERR_INVALID_ARG;
@@ -371,49 +423,27 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
                 const void* W2s, int Fs, int T, int H, int F, int E, int k, float drop_thresh, moe_dtype_t dt,
                 void* y, moe_dtype_t out_dt, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                 int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
-    if (!valid_dtype(dt) || !valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;
-    if (F < 1) return MOE_ERR_INVALID_ARG;
-    int st = check_sizes(T, H, F, E, k);
+    const int st = check_forward(x, Wr, W1, W2, W1s, W2s, Fs, T, H, F, E, k, drop_thresh, dt, y, out_dt);
     if (st != MOE_OK) return st;
-    if ((st = check_drop(drop_thresh, k)) != MOE_OK) return st;
-    if (!x || !Wr || !W1 || !W2 || !y || !ws) return MOE_ERR_INVALID_ARG;
-    if ((W1s == nullptr) != (W2s == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!ws) return MOE_ERR_INVALID_ARG;
     const int fs = W1s ? Fs : 0;
-    if (W1s != nullptr) {
-        if (Fs < 1) return MOE_ERR_INVALID_ARG;
-        if (Fs % 8 != 0) return MOE_ERR_UNSUPPORTED;
-    }
     const FwdLayout L = fwd_layout(T, H, F, E, k, fs, dt);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     char* base = (char*)ws;
-    int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + L.ids);
-    float* w = topk_w ? topk_w : (float*)(base + L.w);
-    int32_t* off = expert_offsets ? expert_offsets : (int32_t*)(base + L.offsets);
-    int32_t* iv = inv ? inv : (int32_t*)(base + L.inv);
-    int32_t* row_token = (int32_t*)(base + L.row_token);
-    int32_t* partial = (int32_t*)(base + L.partial);
-    void* x_perm = base + L.x_perm;
-    float* y_perm = (float*)(base + L.y_perm);
-    float* y_sh = fs > 0 ? (float*)(base + L.y_sh) : nullptr;
-    void* ffn_ws = base + L.ffn;
-    void* route_ws = base + L.route;
-
-    // direct-to-LDS shapes: the W1 launch gathers x rows itself (x_perm is never written) and the W2 launch
-    // writes y_perm as block-scaled fp16 (the combine reads 2 + 1/32 bytes per value instead of 4)
-    const moe::TileCfg cfg = moe::choose_tile((long)T * k, E);
-    const bool gather = moe::ffn_up_gathers(cfg, H, F, (Dtype)dt);
-    const bool packed = moe::ffn_down_packs(cfg, F, H, (Dtype)dt);
-    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, route_ws, stream));
-    if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, off, row_token, iv, partial, !gather, stream)) !=
-        MOE_OK)
-        return st;
-    if ((st = enqueue_ffn(x_perm, gather ? row_token : nullptr, off, W1, W2, T, H, F, E, k, dt, y_perm, x, W1s, W2s, fs,
-                          y_sh, ffn_ws, packed, stream)) != MOE_OK)
-        return st;
-    if (packed)
-        return hip_status(
-            moe::launch_combine_packed(y_perm, (long)T * k, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
-    return hip_status(moe::launch_combine(y_perm, iv, w, y_sh, T, H, k, (Dtype)out_dt, y, stream));
+    FwdBuffers b;
+    b.ids = (int32_t*)(base + L.ids);
+    b.w = (float*)(base + L.w);
+    b.off = (int32_t*)(base + L.offsets);
+    b.inv = (int32_t*)(base + L.inv);
+    b.row_token = (int32_t*)(base + L.row_token);
+    b.partial = (int32_t*)(base + L.partial);
+    b.x_perm = base + L.x_perm;
+    b.y_perm = (float*)(base + L.y_perm);
+    b.y_sh = fs > 0 ? (float*)(base + L.y_sh) : nullptr;
+    b.ffn = base + L.ffn;
+    b.route = base + L.route;
+    return enqueue_forward(x, Wr, bias, W1, W2, W1s, W2s, fs, T, H, F, E, k, drop_thresh, dt, y, out_dt, topk_ids,
+                           topk_w, expert_offsets, inv, b, stream);
 }
 
 size_t moe_fp8_weight_bytes(int E, int K, int N) {
@@ -584,6 +614,18 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
                                     base + L.y, stream));
     return hip_status(
         moe::launch_combine_packed(base + L.y, rows, iv, w, nullptr, T, H, k, (moe::Dtype)out_dt, y, stream));
+}
+
+int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, float* sink, hipStream_t stream) {
+    if (workgroups < 1 || waves_per_workgroup < 1 || waves_per_workgroup > 8 || iters < 1) return MOE_ERR_INVALID_ARG;
+    if (!sink) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_calibrate_mfma(workgroups, waves_per_workgroup, iters, sink, stream));
+}
+
+int moe_calibrate_stream_read(const void* buf, size_t bytes, int workgroups, float* sink, hipStream_t stream) {
+    if (workgroups < 1 || bytes < 16 || bytes % 16 != 0) return MOE_ERR_INVALID_ARG;
+    if (!buf || !sink) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_calibrate_read(buf, (long)bytes, workgroups, sink, stream));
 }
 
 }  // extern "C"
