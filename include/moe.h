@@ -275,6 +275,38 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_forward_noalloc - moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and results (bit-identical y and debug
+ * outputs), with no workspace argument. Its intermediate buffers live in one
+ * static device array of 64 MiB that the library holds on each GPU it runs
+ * on until the process ends; the call allocates and frees nothing.
+ *
+ * Limit: the call returns MOE_ERR_UNSUPPORTED when its buffers do not fit
+ * the 64 MiB. They take, rounded up to 256 bytes each: 16*T*k + 4*(E+1) +
+ * 4*E*ceil(T*k/1024) bytes of routing maps; T*k*F*b bytes of expert
+ * activation (b = 2 for MOE_BF16, 4 for MOE_F32) and T*Fs*b + 4*T*H for a
+ * shared expert; y_perm at T*k*H*(2 + 1/32) bytes on the bf16 shapes whose
+ * W2 launch packs it (moe_forward's precision note), else 4*T*k*H plus
+ * T*k*H*b for x_perm where the W1 launch does not gather rows of x; and the
+ * router's split partial sums (moe_route_workspace_bytes). With H = 2048,
+ * F = 768, bf16, that is about 5.7 KiB per assignment: T*k up to about
+ * 11,000.
+ *
+ * Every call on one GPU uses that GPU's array and leaves the last call's
+ * contents in it; nothing in it needs to start at zero. Calls that overlap
+ * on one GPU (concurrent streams, or threads enqueueing on different
+ * streams) race on the array and must be serialised by the caller.
+ * Arguments, outputs and the other errors are those of moe_forward; a
+ * failure to find the array's device address returns MOE_ERR_HIP.
+ */
+int moe_forward_noalloc(const void* x, const void* Wr, const float* bias, const void* W1,
+                        const void* W2, const void* W1s, const void* W2s, int Fs, int T, int H,
+                        int F, int E, int k, float drop_thresh, moe_dtype_t dt, void* y,
+                        moe_dtype_t out_dt, int32_t* topk_ids, float* topk_w,
+                        int32_t* expert_offsets, int32_t* inv, hipStream_t stream);
+
+/*
  * Low-precision experts: fp8 (OCP e4m3) expert weights.
  *
  * Page 1 ("MoE大模型的智能调度…", www.jsqmd.com/news/1091713), section 4.1

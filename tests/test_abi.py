@@ -324,3 +324,22 @@ def test_binding_rejects_mismatched_tensors(lib):
     raises(ValueError, "must be on the GPU", moe.moe_forward_fp8, x, Wr, None, W1q, s1, W2q, s2, k)
     raises(ValueError, "Wq has shape", moe.moe_quantize_fp8, W1, Wq=W1q[:-1].contiguous())
 
+
+def test_noalloc_limits(lib):
+    """moe_forward_noalloc checks its arguments like moe_forward and refuses, before touching the GPU, a batch
+    whose buffers exceed its 64 MiB scratch array."""
+    N = None
+    bf16 = 1
+
+    def call(T, H, F, E, k, x=_p(), y=_p(), Fs=0, W1s=N, W2s=N, drop=0.0):
+        return lib.moe_forward_noalloc(x, _p(), N, _p(), _p(), W1s, W2s, Fs, T, H, F, E, k, drop, bf16, y, bf16,
+                                       N, N, N, N, N)
+
+    assert call(8192, 2048, 768, 128, 8) == moe.MOE_ERR_UNSUPPORTED      # prefill: ~370 MB of buffers
+    assert call(2048, 2048, 768, 128, 8) == moe.MOE_ERR_UNSUPPORTED      # 16,384 assignments
+    assert call(0, 2048, 768, 128, 8) == moe.MOE_ERR_INVALID_ARG
+    assert call(32, 2048, 768, 128, 8, x=N) == moe.MOE_ERR_INVALID_ARG
+    assert call(32, 2048, 768, 128, 8, y=N) == moe.MOE_ERR_INVALID_ARG
+    assert call(32, 2048, 768, 128, 8, drop=0.5) == moe.MOE_ERR_INVALID_ARG
+    assert call(32, 2048, 768, 128, 8, Fs=64, W1s=_p()) == moe.MOE_ERR_INVALID_ARG   # W2s missing
+    assert call(32, 12, 768, 128, 8) == moe.MOE_ERR_UNSUPPORTED

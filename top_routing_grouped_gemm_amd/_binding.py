@@ -26,7 +26,8 @@ EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_work
            "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_forward_fp8", "moe_mxfp8_weight_bytes",
            "moe_mxfp8_scale_bytes", "moe_quantize_mxfp8", "moe_quantize_mxfp8_rows", "moe_mxfp8_workspace_bytes", "moe_grouped_ffn_mxfp8",
            "moe_grouped_ffn_mxfp8_workspace_bytes",
-           "moe_forward_mxfp8", "moe_calibrate_mfma_bf16", "moe_calibrate_stream_read")
+           "moe_forward_mxfp8", "moe_calibrate_mfma_bf16", "moe_calibrate_stream_read",
+           "moe_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -112,6 +113,9 @@ def load_library(path: Optional[str] = None):
     lib.moe_forward_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, vp,
                                       vp, vp, sz, vp]
     lib.moe_forward_mxfp8.restype = i32
+    lib.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
+                                        vp, vp, vp, vp, vp]
+    lib.moe_forward_noalloc.restype = i32
     lib.moe_calibrate_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
     lib.moe_calibrate_mfma_bf16.restype = i32
     lib.moe_calibrate_stream_read.argtypes = [vp, sz, i32, vp, vp]
@@ -447,6 +451,36 @@ def _mx_weights(W1q, W1_scale, W2q, W2_scale, E, H, F, dev):
     _arg(W1_scale, "W1_scale", (int(lib.moe_mxfp8_scale_bytes(E, H, F)),), torch.uint8, dev)
     _arg(W2q, "W2q", (int(lib.moe_mxfp8_weight_bytes(E, F, H)),), torch.uint8, dev)
     _arg(W2_scale, "W2_scale", (int(lib.moe_mxfp8_scale_bytes(E, F, H)),), torch.uint8, dev)
+
+
+def moe_forward_noalloc(x, Wr, bias, W1, W2, k: int, drop_thresh: float = 0.0, W1s=None, W2s=None,
+                        out_dtype=torch.float32, y=None, topk_ids=None, topk_w=None, expert_offsets=None, inv=None,
+                        stream=None):
+    """moe_forward without a workspace: the intermediate buffers live in the library's static per-GPU scratch
+    array (see include/moe.h for its size limit; calls that overlap on one GPU race on it). Returns y [T,H]."""
+    _arg(x, "x", (None, None), _FLOAT)
+    T, H = x.shape
+    dt, dev = x.dtype, x.device
+    _arg(Wr, "Wr", (H, None), dt, dev)
+    E = Wr.shape[1]
+    _arg(bias, "bias", (E,), torch.float32, dev, optional=True)
+    _arg(W1, "W1", (E, H, None), dt, dev)
+    F = W1.shape[2]
+    _arg(W2, "W2", (E, F, H), dt, dev)
+    if (W1s is None) != (W2s is None):
+        raise ValueError("the shared expert needs both W1s and W2s")
+    Fs = W1s.shape[1] if W1s is not None else 0
+    _arg(W1s, "W1s", (H, None), dt, dev, optional=True)
+    _arg(W2s, "W2s", (Fs, H), dt, dev, optional=W1s is None)
+    y = torch.empty((T, H), dtype=out_dtype, device=dev) if y is None else y
+    _arg(y, "y", (T, H), _FLOAT, dev)
+    _forward_debug_args(T, E, k, topk_ids, topk_w, expert_offsets, inv, dev)
+    st = load_library().moe_forward_noalloc(_ptr(x), _ptr(Wr), _ptr(bias), _ptr(W1), _ptr(W2), _ptr(W1s), _ptr(W2s),
+                                            Fs, T, H, F, E, k, float(drop_thresh), _dt(x), _ptr(y), _dt(y),
+                                            _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(inv),
+                                            _stream(stream))
+    _check(st, "moe_forward_noalloc")
+    return y
 
 
 def moe_fp8_weight_bytes(E: int, K: int, N: int) -> int:

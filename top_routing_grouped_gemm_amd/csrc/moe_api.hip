@@ -2,6 +2,8 @@
 // checks, workspace layout and the launch sequence on the caller's stream.
 #include <math.h>
 
+#include <mutex>
+
 #include "moe.h"
 
 #include "moe_internal.hpp"
@@ -173,7 +175,7 @@ int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* off
     return MOE_OK;
 }
 
-// Device buffers of one forward pass inside the caller workspace.
+// Device buffers of one forward pass (inside a caller workspace or the no-allocation scratch array).
 struct FwdBuffers {
     int32_t *ids, *off, *inv, *row_token, *partial;
     float *w, *y_perm, *y_sh;
@@ -225,12 +227,83 @@ int enqueue_forward(const void* x, const void* Wr, const float* bias, const void
     return hip_status(moe::launch_combine(b.y_perm, iv, w, b.y_sh, T, H, k, (Dtype)out_dt, y, stream));
 }
 
+// Layout of the no-allocation forward inside its scratch array: only the buffers the chosen kernels use
+// (no x_perm when the W1 launch gathers rows of x; y_perm at 2 + 1/32 bytes per value when W2 packs it).
+struct TightLayout {
+    size_t ids, w, offsets, inv, row_token, partial, x_perm, y_perm, y_sh, ffn, route, total;
+    bool gather;
+};
+
+TightLayout tight_layout(int T, int H, int F, int E, int k, int Fs, moe_dtype_t dt) {
+    TightLayout L;
+    const size_t TK = (size_t)T * k;
+    const moe::TileCfg cfg = moe::choose_tile((long)TK, E);
+    L.gather = moe::ffn_up_gathers(cfg, H, F, (Dtype)dt);
+    const bool packed = moe::ffn_down_packs(cfg, F, H, (Dtype)dt);
+    size_t off = 0;
+    auto take = [&](size_t& field, size_t bytes) {
+        field = off;
+        off = align_up(off + bytes);
+    };
+    take(L.ids, TK * sizeof(int32_t));
+    take(L.w, TK * sizeof(float));
+    take(L.offsets, (size_t)(E + 1) * sizeof(int32_t));
+    take(L.inv, TK * sizeof(int32_t));
+    take(L.row_token, TK * sizeof(int32_t));
+    take(L.partial, permute_bytes(T, E, k));
+    take(L.x_perm, L.gather ? 0 : TK * H * elem_bytes(dt));
+    take(L.y_perm, packed ? TK * H * 2 + TK * (H / 32) : TK * H * sizeof(float));
+    take(L.y_sh, Fs > 0 ? (size_t)T * H * sizeof(float) : 0);
+    take(L.ffn, ffn_layout(T, F, k, Fs, dt).total);
+    take(L.route, moe::route_workspace_bytes(T, H, E, (Dtype)dt));
+    L.total = off;
+    return L;
+}
+
 int check_shared(const void* x, const void* W1s, const void* W2s, int Fs, const float* y_shared) {
     if (W1s == nullptr && W2s == nullptr) return MOE_OK;
     if (W1s == nullptr || W2s == nullptr || x == nullptr || y_shared == nullptr) return MOE_ERR_INVALID_ARG;
     if (Fs < 1) return MOE_ERR_INVALID_ARG;
     if (Fs % 8 != 0) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
+}
+
+}  // namespace
+
+// Scratch memory of moe_forward_noalloc, for callers that cannot allocate: one array per GPU that the library
+// runs on, held until the process ends. In host code `scratch` only names the symbol; its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = 64u << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that `stream` belongs to (the current device for the null stream).
+hipError_t scratch_address(hipStream_t stream, char** out) {
+    int dev = -1;
+    hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = (char*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -438,6 +511,33 @@ int moe_forward(const void* x, const void* Wr, const float* bias, const void* W1
     b.row_token = (int32_t*)(base + L.row_token);
     b.partial = (int32_t*)(base + L.partial);
     b.x_perm = base + L.x_perm;
+    b.y_perm = (float*)(base + L.y_perm);
+    b.y_sh = fs > 0 ? (float*)(base + L.y_sh) : nullptr;
+    b.ffn = base + L.ffn;
+    b.route = base + L.route;
+    return enqueue_forward(x, Wr, bias, W1, W2, W1s, W2s, fs, T, H, F, E, k, drop_thresh, dt, y, out_dt, topk_ids,
+                           topk_w, expert_offsets, inv, b, stream);
+}
+
+int moe_forward_noalloc(const void* x, const void* Wr, const float* bias, const void* W1, const void* W2,
+                        const void* W1s, const void* W2s, int Fs, int T, int H, int F, int E, int k,
+                        float drop_thresh, moe_dtype_t dt, void* y, moe_dtype_t out_dt, int32_t* topk_ids,
+                        float* topk_w, int32_t* expert_offsets, int32_t* inv, hipStream_t stream) {
+    const int st = check_forward(x, Wr, W1, W2, W1s, W2s, Fs, T, H, F, E, k, drop_thresh, dt, y, out_dt);
+    if (st != MOE_OK) return st;
+    const int fs = W1s ? Fs : 0;
+    const TightLayout L = tight_layout(T, H, F, E, k, fs, dt);
+    if (L.total > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+    char* base = nullptr;
+    if (scratch_address(stream, &base) != hipSuccess) return MOE_ERR_HIP;
+    FwdBuffers b;
+    b.ids = (int32_t*)(base + L.ids);
+    b.w = (float*)(base + L.w);
+    b.off = (int32_t*)(base + L.offsets);
+    b.inv = (int32_t*)(base + L.inv);
+    b.row_token = (int32_t*)(base + L.row_token);
+    b.partial = (int32_t*)(base + L.partial);
+    b.x_perm = L.gather ? nullptr : base + L.x_perm;
     b.y_perm = (float*)(base + L.y_perm);
     b.y_sh = fs > 0 ? (float*)(base + L.y_sh) : nullptr;
     b.ffn = base + L.ffn;
