@@ -236,7 +236,8 @@ def test_combine_oracle_fed(dev):
 
 
 @pytest.mark.parametrize("T,E", [
-    (777, 37),     # 3108 assignments: count / scan / index kernels
+    (777, 37),     # 3108 assignments: the two-pass dispatch (count+rank, finalize)
+    (9000, 1000),  # 36 chunks x 1000 experts > 32768 counts: count / scan / index kernels
     (256, 37),     # 1024 assignments: the single-workgroup dispatch, at its limit
     (257, 1000),   # 1028 assignments just past it, E near the maximum
     (200, 1000),   # 800 assignments over 1000 experts in one workgroup
@@ -253,6 +254,39 @@ def test_permute_oracle_fed(dev, T, E):
     torch.cuda.synchronize()
     g = dict(ids=ids, w=w, off=off, row_token=row_token, inv=inv, x_perm=x_perm)
     check_routing(g, r, dref, I.x)
+
+
+@pytest.mark.parametrize("T,H,E,k,drop,zipf", [
+    (32, 2048, 128, 8, 0.0, 0.0),     # decode shape: maps built by the router's reduction launch (32 splits)
+    (128, 1024, 256, 8, 0.0, 0.0),    # 1024 assignments, the fused limit; 16 splits, 256 padded experts
+    (1, 4096, 32, 4, 0.0, 0.0),       # one token, 64 splits, 32 padded experts
+    (20, 2048, 64, 6, 0.1, 1.2),      # drops and a skewed bias
+    (200, 1024, 64, 4, 0.0, 0.0),     # 7 token blocks x 16 splits
+    (100, 256, 64, 4, 0.0, 0.0),      # 4 splits: router, then the one-workgroup dispatch
+    (3000, 128, 256, 8, 0.05, 0.0),   # 24,000 assignments: two-pass dispatch
+    (9000, 64, 1000, 4, 0.0, 1.2),    # 36 chunks x 1000 experts: count / scan / index
+])
+def test_forward_routing_maps(dev, T, H, E, k, drop, zipf):
+    """moe_forward's own routing outputs (ids, weights, offsets, inverse map) bit-exact against the oracle on
+    every dispatch path, and y within the layer bound."""
+    I = gen.make_inputs("tiny", T=T, H=H, F=64, E=E, k=k, dtype="bf16", seed=4000 + T, drop=drop, zipf=zipf)
+    _say(f"case T={T} H={H} E={E} k={k} drop={drop} zipf={zipf}")
+    d = gen.to_device(I, dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+    y = None
+    for _ in range(2):  # a second call on the same buffers: the hand-off state carries nothing over
+        y = moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], k, I.drop, topk_ids=ids, topk_w=w,
+                            expert_offsets=off, inv=inv)
+    torch.cuda.synchronize()
+    ref = oracle.forward(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.f64(I.W1()), I.f64(I.W2()), k, I.drop)
+    assert np.array_equal(ids.cpu().numpy(), ref.route.ids), "expert ids differ"
+    assert np.abs(w.cpu().numpy().astype(np.float64) - ref.route.w).max() <= W_TOL
+    assert np.array_equal(off.cpu().numpy(), ref.dispatch.offsets), "expert offsets differ"
+    assert np.array_equal(inv.cpu().numpy(), ref.dispatch.inv), "inverse map differs"
+    check_y(y.double().cpu().numpy(), ref.y)
 
 
 # ------------------------------------------- block-scaled fp16 extremes --
@@ -353,10 +387,13 @@ def test_full_workload(dev, name):
     W1h, W2h = d.pop("W1_host"), d.pop("W2_host")
     ids = torch.empty((I.T, I.k), dtype=torch.int32, device=dev)
     w = torch.empty((I.T, I.k), dtype=torch.float32, device=dev)
+    off1 = torch.empty(I.E + 1, dtype=torch.int32, device=dev)
+    inv1 = torch.empty((I.T, I.k), dtype=torch.int32, device=dev)
     y = moe.moe_forward(d["x"], d["Wr"], d["bias"], d["W1"], d["W2"], I.k, I.drop, W1s=d["W1s"], W2s=d["W2s"],
-                        topk_ids=ids, topk_w=w)
+                        topk_ids=ids, topk_w=w, expert_offsets=off1, inv=inv1)
     g = run_steps(d, I, dev)
-    assert torch.equal(g["ids"], ids)
+    # the one-call dispatch maps (built inside the router launch at decode) equal the step-wise ones
+    assert torch.equal(g["ids"], ids) and torch.equal(g["off"], off1) and torch.equal(g["inv"], inv1)
     A = int(g["off"][-1].item())
     # moe_forward keeps y_perm as block-scaled fp16: within 2^-10 * max|y_perm| of the step-wise (fp32 y_perm) result
     assert float((g["y"] - y).abs().max()) <= 2.0 ** -10 * float(g["y_perm"][:A].abs().max())

@@ -7,17 +7,23 @@
 // token). Section "单机MoE执行流水线": the permute reads token vectors, writes
 // them in expert order and records an inverse map for the combine.
 //
-// Order is fixed by (expert, token), never by atomics (batches of at most
-// 1024 assignments run count, scan and index in one workgroup instead):
-//   count  - each workgroup histograms one chunk of 256 assignments in LDS;
-//   scan   - one workgroup turns the [chunk][expert] histograms into the
-//            first output row of every (chunk, expert) pair and writes the
-//            expert offsets (exclusive prefix sum of the counts);
-//   index  - each workgroup ranks its chunk's assignments within their expert
-//            (wave ballots match equal expert ids, LDS combines the 4 waves)
-//            and writes row_token and inv;
+// Order is fixed by (expert, token), never by atomics. Batches of at most
+// 1024 assignments run count, scan and rank in one workgroup
+// (dispatch_block.hpp). Larger ones take chunks of 1024 assignments:
+//   count_rank - each workgroup histograms its chunk per expert and ranks
+//            every assignment within its expert inside the chunk (wave
+//            ballots match equal expert ids, LDS combines the 16 waves); the
+//            rank goes to inv, the histogram to partial[chunk][expert];
+//   finalize - each workgroup sums the histograms itself (the column sums give
+//            the expert offsets, the sums over earlier chunks its chunk's
+//            first row per expert), so no separate scan launch is needed, and
+//            turns its chunk's ranks into rows: row_token and inv;
 //   copy   - token-major: each token row is read once and written to its k
 //            destination rows (HBM-bound: T*H*b read, A*H*b written).
+// When chunks x experts is too large for every workgroup to read the
+// histograms (more than kFinalizeCounts), one workgroup scans them instead
+// (count, scan, index).
+#include "dispatch_block.hpp"
 #include "moe_common.hpp"
 #include "moe_internal.hpp"
 
@@ -141,11 +147,8 @@ __global__ __launch_bounds__(kDispatchChunk) void index_kernel(const int32_t* __
     }
 }
 
-// All of count, scan and index in one workgroup of 1024 threads, for batches
-// of at most 1024 assignments (decode): thread a ranks assignment a within its
-// expert (wave ballots over the id bits), LDS turns the per-wave counts into
-// wave prefixes and expert offsets, and the same order as the three-kernel
-// path results (expert, then token). Saves two launches where latency, not
+// The whole dispatch of a batch of at most kSmallAssign assignments in one
+// workgroup (dispatch_block.hpp). Saves two launches where latency, not
 // bandwidth, is the cost.
 __global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int32_t* __restrict__ ids,
                                                                       const float* __restrict__ w, int n_assign,
@@ -153,13 +156,22 @@ __global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int3
                                                                       int32_t* __restrict__ offsets,
                                                                       int32_t* __restrict__ row_token,
                                                                       int32_t* __restrict__ inv) {
-    constexpr int NW = kSmallAssign / kWave;
-    __shared__ int wc[NW][kMaxE];  // per-wave counts, then per-wave first rank
-    __shared__ int eoff[kMaxE];    // expert totals, then expert offsets
-    __shared__ int wsum[NW];
+    __shared__ DispatchSmem sm;
+    dispatch_whole(ids, w, n_assign, k, E, ebits, offsets, row_token, inv, sm);
+}
+
+// count_rank: chunk b = blockIdx.x of kDispatchChunk assignments. partial[b][e]
+// = kept assignments of the chunk with expert e; inv[a] = rank of a among the
+// chunk's assignments to its expert (token order), -1 when dropped.
+__global__ __launch_bounds__(kDispatchChunk) void count_rank_kernel(const int32_t* __restrict__ ids,
+                                                                    const float* __restrict__ w, int n_assign, int E,
+                                                                    int ebits, int32_t* __restrict__ partial,
+                                                                    int32_t* __restrict__ inv) {
+    constexpr int NW = kDispatchChunk / kWave;
+    __shared__ int wc[NW][kMaxE];
     const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
-    for (int i = tid; i < NW * E; i += kSmallAssign) (&wc[0][0])[(i / E) * kMaxE + (i % E)] = 0;
-    const int a = tid;
+    for (int i = tid; i < NW * E; i += kDispatchChunk) wc[i / E][i % E] = 0;
+    const int a = blockIdx.x * kDispatchChunk + tid;
     const bool valid = a < n_assign;
     const int id = valid ? ids[a] : 0;
     const bool kept = valid && w[a] != 0.0f && (unsigned)id < (unsigned)E;  // out-of-range ids: dropped
@@ -176,7 +188,8 @@ __global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int3
     __syncthreads();
     if (kept && rank == 0) wc[wv][e] = cnt;
     __syncthreads();
-    for (int x = tid; x < E; x += kSmallAssign) {  // wave prefixes per expert, expert totals
+    int32_t* out = partial + (long)blockIdx.x * E;
+    for (int x = tid; x < E; x += kDispatchChunk) {  // wave prefixes per expert, chunk totals
         int run = 0;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
@@ -184,10 +197,62 @@ __global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int3
             wc[i][x] = run;
             run += c;
         }
-        eoff[x] = run;
+        out[x] = run;
     }
     __syncthreads();
-    const int v = tid < E ? eoff[tid] : 0;  // E <= kMaxE == kSmallAssign: one expert per thread
+    if (valid) inv[a] = kept ? wc[wv][e] + rank : -1;
+}
+
+// finalize: chunk b = blockIdx.x. Thread (g, e) (G = 1024/E groups) sums
+// column e of partial over its share of the chunks, all of them and those
+// before b apart; a scan over e of the column totals gives the expert
+// offsets. Then inv[a] (a rank) becomes offsets[e] + earlier chunks' count of
+// e + rank, and row_token of that row the token of a. Workgroup 0 also writes
+// offsets. Every workgroup reads the nb x E histogram (L2-resident).
+__global__ __launch_bounds__(kDispatchChunk) void finalize_kernel(const int32_t* __restrict__ ids,
+                                                                  const int32_t* __restrict__ partial, int nb,
+                                                                  int n_assign, int k, int E,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ row_token,
+                                                                  int32_t* __restrict__ inv) {
+    constexpr int NW = kDispatchChunk / kWave;
+    __shared__ int gall[kDispatchChunk];  // [G][E] column sums over a group's chunks
+    __shared__ int gbef[kDispatchChunk];  // [G][E] the same over the group's chunks before b
+    __shared__ int base[kMaxE];
+    __shared__ int wsum[NW];
+    const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
+    const int b = blockIdx.x;
+    // this workgroup's assignment and its rank, loaded before the histogram walk
+    const int a = b * kDispatchChunk + tid;
+    const bool valid = a < n_assign;
+    const int lr = valid ? inv[a] : -1;
+    const int id = lr >= 0 ? ids[a] : 0;
+    const int G = (kDispatchChunk / E) > 0 ? (kDispatchChunk / E) : 1;
+    const int bpg = (nb + G - 1) / G;
+    const int e = tid % E, g = tid / E;
+    if (tid < E * G) {
+        const int b0 = g * bpg, b1 = min(nb, b0 + bpg);
+        int s_all = 0, s_bef = 0;
+        for (int c0 = b0; c0 < b1; c0 += 8) {  // 8 independent loads in flight
+            int c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = (c0 + u < b1) ? partial[(long)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s_all += c[u];
+                s_bef += (c0 + u < b) ? c[u] : 0;
+            }
+        }
+        gall[g * E + e] = s_all;
+        gbef[g * E + e] = s_bef;
+    }
+    __syncthreads();
+    int v = 0, bef = 0;
+    if (tid < E)
+        for (int i = 0; i < G; ++i) {
+            v += gall[i * E + tid];
+            bef += gbef[i * E + tid];
+        }
     const int incl = wave_incl_scan(v);
     if (l == kWave - 1) wsum[wv] = incl;
     __syncthreads();
@@ -195,26 +260,26 @@ __global__ __launch_bounds__(kSmallAssign) void dispatch_small_kernel(const int3
     for (int i = 0; i < wv; ++i) wbase += wsum[i];
     const int excl = wbase + incl - v;
     if (tid < E) {
-        eoff[tid] = excl;
-        offsets[tid] = excl;
-    }
-    if (tid == E - 1) offsets[E] = excl + v;
-    __syncthreads();
-    if (valid) {
-        if (kept) {
-            const int r = eoff[e] + wc[wv][e] + rank;
-            row_token[r] = a / k;
-            inv[a] = r;
-        } else {
-            inv[a] = -1;
+        base[tid] = excl + bef;
+        if (b == 0) {
+            offsets[tid] = excl;
+            if (tid == E - 1) offsets[E] = excl + v;
         }
+    }
+    __syncthreads();
+    if (lr >= 0) {
+        const int r = base[id] + lr;
+        row_token[r] = a / k;
+        inv[a] = r;
     }
 }
 
 // Token-major row copy: each wave takes TPW tokens, reads each token row of
 // x once (all TPW rows' loads in flight before any store) and writes it to
 // the k destination rows its assignments got (inv; dropped slots: none), so x
-// is read T*H*b bytes once instead of once per assignment.
+// is read T*H*b bytes once instead of once per assignment. The x loads are
+// non-temporal (read once; prefill copy 52 -> 45 us); the stores are not,
+// since the W1 launch reads x_perm right after.
 template <int TPW, int VPL>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4* __restrict__ x, const int32_t* __restrict__ inv,
                                                            int T, int k, int V, u32x4* __restrict__ out) {
@@ -228,7 +293,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4* __restri
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
                 const int c = c0 + u * kWave + l;
-                if (t0 + i < T && c < V) v[i][u] = x[(t0 + i) * V + c];
+                if (t0 + i < T && c < V) v[i][u] = __builtin_nontemporal_load(&x[(t0 + i) * V + c]);
             }
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -256,10 +321,25 @@ hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E,
 
 hipError_t launch_dispatch_small(const int32_t* ids, const float* w, int n_assign, int k, int E, int32_t* offsets,
                                  int32_t* row_token, int32_t* inv, hipStream_t s) {
-    int ebits = 0;
-    while ((1 << ebits) < E) ++ebits;
-    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallAssign), 0, s, ids, w, n_assign, k, E, ebits, offsets,
-                       row_token, inv);
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallAssign), 0, s, ids, w, n_assign, k, E,
+                       expert_bits(E), offsets, row_token, inv);
+    return hipGetLastError();
+}
+
+bool dispatch_two_pass(long n_assign, int E) { return (long)dispatch_blocks(n_assign) * E <= kFinalizeCounts; }
+
+hipError_t launch_count_rank(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial, int32_t* inv,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(count_rank_kernel, dim3(dispatch_blocks(n_assign)), dim3(kDispatchChunk), 0, s, ids, w,
+                       n_assign, E, expert_bits(E), partial, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const int32_t* ids, const int32_t* partial, int n_assign, int k, int E, int32_t* offsets,
+                           int32_t* row_token, int32_t* inv, hipStream_t s) {
+    const int nb = dispatch_blocks(n_assign);
+    hipLaunchKernelGGL(finalize_kernel, dim3(nb), dim3(kDispatchChunk), 0, s, ids, partial, nb, n_assign, k, E,
+                       offsets, row_token, inv);
     return hipGetLastError();
 }
 
@@ -270,10 +350,8 @@ hipError_t launch_scan(int32_t* partial, int n_blocks, int E, int32_t* offsets, 
 
 hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* partial, int n_assign, int k, int E,
                         int32_t* row_token, int32_t* inv, hipStream_t s) {
-    int ebits = 0;
-    while ((1 << ebits) < E) ++ebits;
     const int nb = dispatch_blocks(n_assign);
-    hipLaunchKernelGGL(index_kernel, dim3(nb), dim3(kDispatchChunk), 0, s, ids, w, partial, n_assign, k, E, ebits,
+    hipLaunchKernelGGL(index_kernel, dim3(nb), dim3(kDispatchChunk), 0, s, ids, w, partial, n_assign, k, E, expert_bits(E),
                        row_token, inv);
     return hipGetLastError();
 }

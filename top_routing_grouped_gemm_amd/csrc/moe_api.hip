@@ -137,6 +137,9 @@ int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, in
     const int n = T * k;
     if (n <= moe::kSmallAssign) {
         MOE_TRY(moe::launch_dispatch_small(ids, w, n, k, E, offsets, row_token, inv, s));
+    } else if (moe::dispatch_two_pass(n, E)) {
+        MOE_TRY(moe::launch_count_rank(ids, w, n, E, partial, inv, s));
+        MOE_TRY(moe::launch_finalize(ids, partial, n, k, E, offsets, row_token, inv, s));
     } else {
         MOE_TRY(moe::launch_count(ids, w, n, E, partial, s));
         MOE_TRY(moe::launch_scan(partial, moe::dispatch_blocks(n), E, offsets, s));
@@ -144,6 +147,14 @@ int enqueue_permute(const void* x, const int32_t* ids, const float* w, int T, in
     }
     if (copy_rows) MOE_TRY(moe::launch_copy_rows(x, inv, T, k, (int)(H * elem_bytes(dt)), x_perm, s));
     return MOE_OK;
+}
+
+// Router, then the dispatch maps (+ the row copy when copy_rows).
+int enqueue_route_permute(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k, float drop,
+                          moe_dtype_t dt, int32_t* ids, float* w, void* route_ws, void* x_perm, int32_t* offsets,
+                          int32_t* row_token, int32_t* inv, int32_t* partial, bool copy_rows, hipStream_t s) {
+    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop, (Dtype)dt, ids, w, route_ws, s));
+    return enqueue_permute(x, ids, w, T, H, E, k, dt, x_perm, offsets, row_token, inv, partial, copy_rows, s);
 }
 
 // row_token != NULL: the W1 launch gathers rows of x through row_token instead of reading x_perm.
@@ -214,9 +225,8 @@ int enqueue_forward(const void* x, const void* Wr, const float* bias, const void
     const bool gather = moe::ffn_up_gathers(cfg, H, F, (Dtype)dt);
     const bool packed = moe::ffn_down_packs(cfg, F, H, (Dtype)dt);
     int st;
-    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, (Dtype)dt, ids, w, b.route, stream));
-    if ((st = enqueue_permute(x, ids, w, T, H, E, k, dt, b.x_perm, off, b.row_token, iv, b.partial, !gather,
-                              stream)) != MOE_OK)
+    if ((st = enqueue_route_permute(x, Wr, bias, T, H, E, k, drop_thresh, dt, ids, w, b.route, b.x_perm, off,
+                                    b.row_token, iv, b.partial, !gather, stream)) != MOE_OK)
         return st;
     if ((st = enqueue_ffn(b.x_perm, gather ? b.row_token : nullptr, off, W1, W2, T, H, F, E, k, dt, b.y_perm, x, W1s,
                           W2s, fs, b.y_sh, b.ffn, packed, stream)) != MOE_OK)
@@ -605,9 +615,8 @@ int moe_forward_fp8(const void* x, const void* Wr, const float* bias, const uint
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
     // the W1 launch gathers x rows through row_token (no permuted copy); the W2 launch writes block-scaled fp16 y_perm
-    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, moe::kBF16, ids, w, base + L.route, stream));
-    if ((st = enqueue_permute(x, ids, w, T, H, E, k, MOE_BF16, nullptr, off, row_token, iv, partial, false,
-                              stream)) != MOE_OK)
+    if ((st = enqueue_route_permute(x, Wr, bias, T, H, E, k, drop_thresh, MOE_BF16, ids, w, base + L.route, nullptr,
+                                    off, row_token, iv, partial, false, stream)) != MOE_OK)
         return st;
     MOE_TRY(moe::launch_ffn_up_fp8(x, row_token, off, E, rows, W1q, W1_scale, H, F, cfg, h, stream));
     MOE_TRY(moe::launch_ffn_down_fp8(h, off, E, rows, W2q, W2_scale, F, H, cfg, true, y_planes, rows, stream));
@@ -703,9 +712,8 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
     uint8_t* xq = (uint8_t*)(base + L.xq);
     uint8_t* xs = (uint8_t*)(base + L.xs);
     // the router keeps bf16 x; the experts read x quantised to MX once per token (gathered by the W1 launch)
-    MOE_TRY(moe::launch_route(x, Wr, bias, T, H, E, k, drop_thresh, moe::kBF16, ids, w, base + L.route, stream));
-    if ((st = enqueue_permute(x, ids, w, T, H, E, k, MOE_BF16, nullptr, off, row_token, iv,
-                              (int32_t*)(base + L.partial), false, stream)) != MOE_OK)
+    if ((st = enqueue_route_permute(x, Wr, bias, T, H, E, k, drop_thresh, MOE_BF16, ids, w, base + L.route, nullptr,
+                                    off, row_token, iv, (int32_t*)(base + L.partial), false, stream)) != MOE_OK)
         return st;
     MOE_TRY(moe::launch_quantize_mx_rows(x, T, H, moe::kBF16, xq, xs, stream));
     MOE_TRY(moe::launch_ffn_up_mx(xq, xs, T, row_token, off, E, (int)rows, W1q, W1_scale, H, F, base + L.hq,

@@ -39,7 +39,17 @@ hipError_t launch_capacity_select(const float* logits, int ld, int T, int E, int
 hipError_t launch_route(const void* x, const void* Wr, const float* bias, int T, int H, int E, int k,
                         float drop, Dtype dt, int32_t* ids, float* w, void* ws, hipStream_t s);
 
-// Dispatch: per-chunk expert histograms -> scan -> stable ranks -> row copy.
+// Dispatch of more than kSmallAssign assignments, two passes: per-chunk
+// expert histograms and in-chunk ranks (inv holds the rank in between), then
+// every chunk's rows from the histograms. Used while chunks x experts <=
+// kFinalizeCounts (each finalize workgroup reads all the counts).
+constexpr long kFinalizeCounts = 32768;
+bool dispatch_two_pass(long n_assign, int E);
+hipError_t launch_count_rank(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial, int32_t* inv,
+                             hipStream_t s);
+hipError_t launch_finalize(const int32_t* ids, const int32_t* partial, int n_assign, int k, int E, int32_t* offsets,
+                           int32_t* row_token, int32_t* inv, hipStream_t s);
+// Larger batches: per-chunk expert histograms -> one-workgroup scan -> stable ranks.
 hipError_t launch_count(const int32_t* ids, const float* w, int n_assign, int E, int32_t* partial,
                         hipStream_t s);
 hipError_t launch_scan(int32_t* partial, int n_blocks, int E, int32_t* offsets, hipStream_t s);
