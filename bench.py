@@ -98,6 +98,9 @@ def stage_times(d, I, reps):
     def combine():
         moe.moe_combine(y_perm, inv, w, y_shared=y_sh, y=y)
 
+    def ffn_fused():  # the same routed FFN in one launch with h kept in LDS (shapes it covers only)
+        moe.moe_grouped_ffn_fused(x_perm, off, d["W1"], d["W2"], T, k, y_perm=y_perm)
+
     route()
     permute()
     torch.cuda.synchronize()
@@ -105,10 +108,12 @@ def stage_times(d, I, reps):
     counts = (off[1:] - off[:-1]).cpu()
     stages = (("route", route), ("permute", permute), ("grouped_ffn", ffn), ("combine", combine))
     out = {name: event_time_ms(fn, reps, s) for name, fn in stages}
+    fused_ok = (d["x"].dtype == torch.bfloat16 and not I.Fs and F % 256 == 0 and F <= 768 and H % 256 == 0)
+    fused = event_time_ms(ffn_fused, reps, s) if fused_ok else None
     ev = evict_buffer()
     cold = {name: event_time_ms(fn, reps, s, evict=ev) for name, fn in stages}
     del ev
-    return out, cold, A, counts
+    return out, cold, A, counts, fused
 
 
 def bytes_model(I, A, experts_hit, out_bytes=4):
@@ -191,7 +196,7 @@ def run_workload(name, steps, warmup, stage_reps, graph=False):
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t) * 1e3 / steps
         del g
-    st, cold, A, counts = stage_times(d, I, stage_reps)
+    st, cold, A, counts, fused = stage_times(d, I, stage_reps)
     hit = int((counts > 0).sum())
     flops = 4.0 * A * I.H * I.F + 4.0 * I.T * I.H * I.Fs  # routed experts + shared expert
     byts = bytes_model(I, A, hit)
@@ -218,6 +223,11 @@ def run_workload(name, steps, warmup, stage_reps, graph=False):
         "weight_stream_gbs": round((hit * 2 * I.H * I.F + 2 * I.H * I.Fs) * I.elem_bytes
                                    / (st["grouped_ffn"] * 1e-3) / 1e9, 1),
         "grouped_ffn_flops": flops,
+        **({"grouped_ffn_h_on_chip": {
+            "ms": round(fused, 5), "tflops": round(flops / (fused * 1e-3) / 1e12, 1),
+            "vs_two_launch": round(st["grouped_ffn"] / fused, 3),
+            "note": "moe_grouped_ffn_fused: W1, SiLU and W2 in one launch, h in LDS (64-row tiles); vs_two_launch "
+                    "> 1 means faster than moe_grouped_ffn"}} if fused is not None else {}),
         "algorithmic_bytes": byts,
         "method_bytes": byts_m,
         "bytes_note": "algorithmic_bytes: each array once in the formats the step-wise calls use (fp32 y_perm, "

@@ -230,6 +230,32 @@ int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const voi
                     float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_grouped_ffn_fused - the grouped FFN in one launch with the hidden
+ * activation h kept on chip (never written to device memory).
+ *
+ * Page 3, section "单机MoE执行流水线": kernel fusion merges operators that
+ * would run as separate launches, so the intermediate activation need not go
+ * back to memory; a fused kernel covers only some data types and shapes, and
+ * the rest use the modular path.
+ *
+ *   y_perm[r] = silu(x_perm[r] @ W1[e]) @ W2[e]   for r in group e (fp32 out,
+ *               bf16 products, fp32 accumulation, h rounded to bf16 as in
+ *               moe_grouped_ffn)
+ *
+ * Covers dt = MOE_BF16 with F % 256 == 0, F <= 768 and H % 256 == 0 (each
+ * 64-row tile's h, 64 x F bf16, must fit in LDS beside its weight ring);
+ * other shapes return MOE_ERR_UNSUPPORTED (use moe_grouped_ffn). No
+ * workspace and no shared expert. Arguments as moe_grouped_ffn: x_perm
+ * [T*k,H], expert_offsets [E+1], W1 [E,H,F], W2 [E,F,H], y_perm [T*k,H] fp32
+ * (rows >= expert_offsets[E] untouched). Kept beside the two-launch path for
+ * comparison: every 64-row tile streams its expert's whole W1 and W2, which
+ * at prefill costs more than the h round trip it saves.
+ */
+int moe_grouped_ffn_fused(const void* x_perm, const int32_t* expert_offsets, const void* W1,
+                          const void* W2, int T, int H, int F, int E, int k, moe_dtype_t dt,
+                          float* y_perm, hipStream_t stream);
+
+/*
  * moe_combine - unpermute and route-weight combine.
  *
  * Page 1, section 2.2, fusion layer: the output is the gate-weighted sum of

@@ -343,3 +343,20 @@ def test_noalloc_limits(lib):
     assert call(32, 2048, 768, 128, 8, drop=0.5) == moe.MOE_ERR_INVALID_ARG
     assert call(32, 2048, 768, 128, 8, Fs=64, W1s=_p()) == moe.MOE_ERR_INVALID_ARG   # W2s missing
     assert call(32, 12, 768, 128, 8) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_grouped_ffn_fused_limits(lib):
+    """The on-chip-h grouped FFN refuses, before any launch, the shapes whose h does not fit (F > 768, F % 256 != 0,
+    H % 256 != 0) and non-bf16 operands."""
+    N = None
+
+    def call(T=64, H=256, F=256, E=4, k=2, dt=1, x=_p(), y=_p()):
+        return lib.moe_grouped_ffn_fused(x, _p(), _p(), _p(), T, H, F, E, k, dt, y, N)
+
+    assert call(F=1024) == moe.MOE_ERR_UNSUPPORTED
+    assert call(F=320) == moe.MOE_ERR_UNSUPPORTED
+    assert call(H=384) == moe.MOE_ERR_UNSUPPORTED
+    assert call(dt=0) == moe.MOE_ERR_UNSUPPORTED
+    assert call(x=N) == moe.MOE_ERR_INVALID_ARG
+    assert call(y=N) == moe.MOE_ERR_INVALID_ARG
+    assert call(T=0) == moe.MOE_ERR_INVALID_ARG

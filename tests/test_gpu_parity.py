@@ -289,6 +289,33 @@ def test_forward_routing_maps(dev, T, H, E, k, drop, zipf):
     check_y(y.double().cpu().numpy(), ref.y)
 
 
+@pytest.mark.parametrize("T,H,F,E,k,zipf", [
+    (300, 256, 256, 5, 2, 0.0),      # ragged 64-row tiles, one 256-column chunk per phase
+    (700, 512, 512, 8, 2, 1.2),      # skewed groups (some experts empty), two chunks of F
+    (1024, 256, 768, 4, 3, 0.0),     # F = 768: the largest h (64 x 768 bf16 = 96 KB of LDS)
+    (37, 256, 256, 16, 4, 0.0),      # few rows: most groups below one tile, some empty
+])
+def test_grouped_ffn_fused(dev, T, H, F, E, k, zipf):
+    """The one-launch grouped FFN with h kept in LDS: y_perm against the oracle (layer bound) and against the
+    two-launch moe_grouped_ffn, which rounds h to bf16 the same way and accumulates every output over k in the
+    same order (printed: the largest difference)."""
+    I = gen.make_inputs("tiny", T=T, H=H, F=F, E=E, k=k, dtype="bf16", seed=5000 + T, zipf=zipf)
+    _say(f"case T={T} H={H} F={F} E={E} k={k} zipf={zipf}")
+    d = gen.to_device(I, dev)
+    ids, w = moe.moe_route(d["x"], d["Wr"], d["bias"], k, I.drop)
+    x_perm, off, row_token, inv = moe.moe_permute(d["x"], ids, w, E)
+    y_two, _ = moe.moe_grouped_ffn(x_perm, off, d["W1"], d["W2"], T, k)
+    y_one = moe.moe_grouped_ffn_fused(x_perm, off, d["W1"], d["W2"], T, k)
+    torch.cuda.synchronize()
+    A = int(off[-1].item())
+    ref = oracle.forward(I.f64(I.x), I.f64(I.Wr), I.bias_f64(), I.f64(I.W1()), I.f64(I.W2()), k, I.drop)
+    check_y(y_one[:A].double().cpu().numpy(), ref.y_perm[:A])
+    diff = float((y_one[:A] - y_two[:A]).abs().max()) if A else 0.0
+    scale = float(y_two[:A].abs().max()) if A else 1.0
+    _say(f"fused vs two-launch: max |diff| {diff:.3e} (max |y_perm| {scale:.3e})")
+    assert diff <= 1e-5 * scale
+
+
 # ------------------------------------------- block-scaled fp16 extremes --
 def test_scaled16_dynamic_range(dev):
     """The one-call layer's block-scaled fp16 y_perm at the ends of its range. W2 columns are scaled so that

@@ -27,7 +27,7 @@ EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_work
            "moe_mxfp8_scale_bytes", "moe_quantize_mxfp8", "moe_quantize_mxfp8_rows", "moe_mxfp8_workspace_bytes", "moe_grouped_ffn_mxfp8",
            "moe_grouped_ffn_mxfp8_workspace_bytes",
            "moe_forward_mxfp8", "moe_calibrate_mfma_bf16", "moe_calibrate_stream_read",
-           "moe_forward_noalloc")
+           "moe_forward_noalloc", "moe_grouped_ffn_fused")
 
 
 class MoEError(RuntimeError):
@@ -82,6 +82,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_grouped_ffn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, sz,
                                     vp]
     lib.moe_grouped_ffn.restype = i32
+    lib.moe_grouped_ffn_fused.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.moe_grouped_ffn_fused.restype = i32
     lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
     lib.moe_combine.restype = i32
     lib.moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp, vp,
@@ -337,6 +339,23 @@ def moe_grouped_ffn(x_perm, expert_offsets, W1, W2, T: int, k: int, y_perm=None,
                                         _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_grouped_ffn")
     return y_perm, y_shared
+
+
+def moe_grouped_ffn_fused(x_perm, expert_offsets, W1, W2, T: int, k: int, y_perm=None, stream=None):
+    """Grouped FFN in one launch with h kept on chip (bf16, F % 256 == 0, F <= 768, H % 256 == 0).
+    Returns y_perm [T*k,H] fp32; other shapes raise MoEError (MOE_ERR_UNSUPPORTED)."""
+    _arg(x_perm, "x_perm", (T * k, None), _FLOAT)
+    dt, dev = x_perm.dtype, x_perm.device
+    _arg(W1, "W1", (None, x_perm.shape[1], None), dt, dev)
+    E, H, F = W1.shape
+    _arg(W2, "W2", (E, F, H), dt, dev)
+    _arg(expert_offsets, "expert_offsets", (E + 1,), torch.int32, dev)
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device=dev) if y_perm is None else y_perm
+    _arg(y_perm, "y_perm", (T * k, H), torch.float32, dev)
+    st = load_library().moe_grouped_ffn_fused(_ptr(x_perm), _ptr(expert_offsets), _ptr(W1), _ptr(W2), T, H, F, E, k,
+                                              _dt(x_perm), _ptr(y_perm), _stream(stream))
+    _check(st, "moe_grouped_ffn_fused")
+    return y_perm
 
 
 def moe_pad_dispatch(x, topk_ids, expert_offsets, row_token, inv, E: int, C: int, x_pad=None, inv_pad=None,

@@ -10,9 +10,6 @@
 // its rank among them; LDS turns the per-wave counts into wave prefixes per
 // expert and the expert totals into offsets (exclusive scan). The resulting
 // order is (expert, token), the same as the multi-workgroup path.
-//
-// Used by the one-workgroup dispatch kernel and by the router's reduction
-// kernel, whose last workgroup runs it once every token's top-k is written.
 #pragma once
 
 #include "moe_common.hpp"

@@ -493,6 +493,17 @@ int moe_grouped_ffn(const void* x_perm, const int32_t* expert_offsets, const voi
                        ws, false, stream);
 }
 
+int moe_grouped_ffn_fused(const void* x_perm, const int32_t* expert_offsets, const void* W1, const void* W2, int T,
+                          int H, int F, int E, int k, moe_dtype_t dt, float* y_perm, hipStream_t stream) {
+    if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+    if (F < 1) return MOE_ERR_INVALID_ARG;
+    const int st = check_sizes(T, H, F, E, k);
+    if (st != MOE_OK) return st;
+    if (!x_perm || !expert_offsets || !W1 || !W2 || !y_perm) return MOE_ERR_INVALID_ARG;
+    if (!moe::ffn_fused_ok(H, F, (Dtype)dt)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_ffn_fused(x_perm, expert_offsets, E, T * k, W1, W2, H, F, y_perm, stream));
+}
+
 int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, const float* y_shared, int T, int H,
                 int k, moe_dtype_t out_dt, void* y, hipStream_t stream) {
     if (!valid_dtype(out_dt)) return MOE_ERR_INVALID_ARG;

@@ -74,6 +74,11 @@ hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed
                          const void* W1, int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s);
 hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
                            const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s);
+// W1 -> SiLU -> W2 in one launch with h kept in LDS (64-row tiles; bf16, F % 256 == 0, F <= 768,
+// H % 256 == 0): y_perm [max_rows][H] fp32.
+bool ffn_fused_ok(int H, int F, Dtype dt);
+hipError_t launch_ffn_fused(const void* x_perm, const int32_t* offsets, int E, int max_rows, const void* W1,
+                            const void* W2, int H, int F, float* y_perm, hipStream_t s);
 // Row capacity for the k-blocked h (the large direct-to-LDS shape with bf16
 // and F % 32 == 0), or 0 for row-major.
 long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt);
