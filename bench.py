@@ -3,10 +3,17 @@
 One step = one moe_forward over the whole prefill batch (T=8192 tokens,
 H=2048, F=768, E=128 routed experts, top-8, bf16 operands, fp32 accumulation),
 inputs resident in HBM. Prints ONE JSON line with the layer's tokens/s, the
-grouped FFN's MFMA roofline fraction, per-stage times, the decode-shaped layer
-(T=32) next to it, and the fp64 CPU oracle timed on the host as a baseline.
+grouped FFN's MFMA roofline (live HIP-event timing, the vendor library's dense
+rate on the same FLOPs beside it), per-stage times with and without the MALL
+evicted and their HBM fractions, the grouped FFN with h kept on chip beside
+the two-launch one, the decode-shaped layer (T=32; weight stream, graph
+replay, fp8 and MX fp8 experts), the Mixtral-like layer with a shared expert
+and the skewed-routing layer, ceilings measured on the box (bare MFMA loop,
+streaming read, a large library GEMM), and the fp64 CPU oracle timed on the
+host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+       python bench.py --only {tiny,decode,prefill,mixtral_shared,skew}   (one workload's record)
 """
 from __future__ import annotations
 
@@ -504,7 +511,13 @@ def calibration():
         ms = event_time_ms(lambda: moe.moe_calibrate_stream_read(buf, wg, sink), 5, s)
         out[f"stream_read_{wg}_workgroups_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     del buf
-    out["note"] = "bare-loop and streaming-read ceilings (library calibration kernels); context for the fractions"
+    # the vendor library on a large square bf16 GEMM: the chip's practical dense-GEMM rate, against which the
+    # library's rate on this layer's shapes (roofline.library_dense_gemm) shows what the shapes themselves cost
+    n = 8192
+    sq = library_dense_gemm(n, n, n)
+    out["library_square_gemm_8192_tflops"] = round(2.0 * n ** 3 / (sq * 1e-3) / 1e12, 1)
+    out["note"] = ("bare-loop and streaming-read ceilings (library calibration kernels) and the vendor library's "
+                   "8192^3 bf16 GEMM; context for the fractions")
     return out
 
 
