@@ -511,13 +511,25 @@ def calibration():
         ms = event_time_ms(lambda: moe.moe_calibrate_stream_read(buf, wg, sink), 5, s)
         out[f"stream_read_{wg}_workgroups_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     del buf
+    # the grouped FFN's 256x256 k-step alone, with its 32 KB-per-step direct-to-LDS feed from an L2-resident
+    # 4 MiB span, and that feed alone: the main loop's own ceiling with and without the feed
+    src = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    steps = 512
+    ks = {}
+    for mode, key in ((0, "no_feed_tflops"), (1, "with_feed_tflops"), (2, "feed_only_tbs")):
+        work = moe.moe_calibrate_gemm_kstep(mode, 256, steps, src=src, sink=sink)
+        ms = event_time_ms(lambda: moe.moe_calibrate_gemm_kstep(mode, 256, steps, src=src, sink=sink), 5, s)
+        ks[key] = round(work / (ms * 1e-3) / 1e12, 1)
+    out["gemm_kstep_256x256"] = ks
+    del src, sink
     # the vendor library on a large square bf16 GEMM: the chip's practical dense-GEMM rate, against which the
     # library's rate on this layer's shapes (roofline.library_dense_gemm) shows what the shapes themselves cost
     n = 8192
     sq = library_dense_gemm(n, n, n)
     out["library_square_gemm_8192_tflops"] = round(2.0 * n ** 3 / (sq * 1e-3) / 1e12, 1)
-    out["note"] = ("bare-loop and streaming-read ceilings (library calibration kernels) and the vendor library's "
-                   "8192^3 bf16 GEMM; context for the fractions")
+    out["note"] = ("bare-loop, streaming-read and GEMM k-step ceilings (library calibration kernels) and the vendor "
+                   "library's 8192^3 bf16 GEMM; context for the fractions")
     return out
 
 

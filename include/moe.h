@@ -458,11 +458,23 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
  * moe_calibrate_stream_read: reads `bytes` (a multiple of 16) of `buf` once
  *   with 16-byte loads from `workgroups` workgroups of 256 threads, one float
  *   per thread to sink[workgroups * 256].
- * Both return MOE_ERR_INVALID_ARG for sizes outside these ranges or a null
+ * moe_calibrate_gemm_kstep: `workgroups` workgroups of 512 threads each run
+ *   `steps` k-steps of the grouped FFN's 256x256 tile (the main loop of its
+ *   large tiles: 8 waves, a 4-stage ring of 32 KB stages, 16-byte and
+ *   transpose LDS reads, 16 v_mfma_f32_32x32x16_bf16 per wave, one barrier),
+ *   i.e. workgroups * steps * 4194304 FLOP, without the tile's epilogue.
+ *   mode 0: on the LDS contents alone (src unused, may be NULL); mode 1: each
+ *   step's stage also filled by 16-byte direct-to-LDS loads from src at byte
+ *   offsets modulo span (span >= 32768, a multiple of 16; the whole span is
+ *   read), 32 KB per step per workgroup; mode 2: those loads alone. One float
+ *   per thread to sink[workgroups * 512].
+ * All return MOE_ERR_INVALID_ARG for sizes outside these ranges or a null
  * pointer, MOE_ERR_HIP if the launch fails.
  */
 int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, float* sink, hipStream_t stream);
 int moe_calibrate_stream_read(const void* buf, size_t bytes, int workgroups, float* sink, hipStream_t stream);
+int moe_calibrate_gemm_kstep(const void* src, size_t span, int workgroups, int steps, int mode, float* sink,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -360,3 +360,14 @@ def test_grouped_ffn_fused_limits(lib):
     assert call(x=N) == moe.MOE_ERR_INVALID_ARG
     assert call(y=N) == moe.MOE_ERR_INVALID_ARG
     assert call(T=0) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_calibrate_gemm_kstep_rejects(lib):
+    """The k-step calibration aid refuses bad modes and feed spans before any launch."""
+    N = None
+    assert lib.moe_calibrate_gemm_kstep(N, 0, 256, 16, 3, _p(), N) == moe.MOE_ERR_INVALID_ARG     # no mode 3
+    assert lib.moe_calibrate_gemm_kstep(N, 0, 256, 16, 1, _p(), N) == moe.MOE_ERR_INVALID_ARG     # feed needs src
+    assert lib.moe_calibrate_gemm_kstep(_p(), 16384, 256, 16, 1, _p(), N) == moe.MOE_ERR_INVALID_ARG  # span < 32 KB
+    assert lib.moe_calibrate_gemm_kstep(_p(), 40008, 256, 16, 2, _p(), N) == moe.MOE_ERR_INVALID_ARG  # span % 16 != 0
+    assert lib.moe_calibrate_gemm_kstep(N, 0, 0, 16, 0, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calibrate_gemm_kstep(N, 0, 256, 16, 0, N, N) == moe.MOE_ERR_INVALID_ARG

@@ -27,7 +27,7 @@ EXPORTS = ("moe_strerror", "moe_version", "moe_workspace_bytes", "moe_route_work
            "moe_mxfp8_scale_bytes", "moe_quantize_mxfp8", "moe_quantize_mxfp8_rows", "moe_mxfp8_workspace_bytes", "moe_grouped_ffn_mxfp8",
            "moe_grouped_ffn_mxfp8_workspace_bytes",
            "moe_forward_mxfp8", "moe_calibrate_mfma_bf16", "moe_calibrate_stream_read",
-           "moe_forward_noalloc", "moe_grouped_ffn_fused")
+           "moe_forward_noalloc", "moe_grouped_ffn_fused", "moe_calibrate_gemm_kstep")
 
 
 class MoEError(RuntimeError):
@@ -122,6 +122,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_calibrate_mfma_bf16.restype = i32
     lib.moe_calibrate_stream_read.argtypes = [vp, sz, i32, vp, vp]
     lib.moe_calibrate_stream_read.restype = i32
+    lib.moe_calibrate_gemm_kstep.argtypes = [vp, sz, i32, i32, i32, vp, vp]
+    lib.moe_calibrate_gemm_kstep.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -678,3 +680,15 @@ def moe_calibrate_stream_read(buf, workgroups: int, sink=None, stream=None) -> i
     _check(load_library().moe_calibrate_stream_read(_ptr(buf), nbytes, workgroups, _ptr(sink), _stream(stream)),
            "moe_calibrate_stream_read")
     return nbytes
+
+
+def moe_calibrate_gemm_kstep(mode: int, workgroups: int, steps: int, src=None, sink=None, stream=None) -> int:
+    """The grouped FFN's 256x256 k-step repeated (measurement aid): mode 0 without global memory, 1 with its
+    32 KB-per-step direct-to-LDS feed from src (offsets modulo src's size), 2 the feed alone.
+    Returns the FLOP count of the launch (modes 0 and 1) or the bytes fed (mode 2)."""
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device="cuda") if sink is None else sink
+    _arg(sink, "sink", (workgroups * 512,), torch.float32)
+    span = src.numel() * src.element_size() if src is not None else 0
+    _check(load_library().moe_calibrate_gemm_kstep(_ptr(src), span, workgroups, steps, mode, _ptr(sink),
+                                                   _stream(stream)), "moe_calibrate_gemm_kstep")
+    return workgroups * steps * 32768 if mode == 2 else workgroups * steps * 4194304

@@ -747,4 +747,12 @@ int moe_calibrate_stream_read(const void* buf, size_t bytes, int workgroups, flo
     return hip_status(moe::launch_calibrate_read(buf, (long)bytes, workgroups, sink, stream));
 }
 
+int moe_calibrate_gemm_kstep(const void* src, size_t span, int workgroups, int steps, int mode, float* sink,
+                             hipStream_t stream) {
+    if (workgroups < 1 || steps < 1 || mode < 0 || mode > 2) return MOE_ERR_INVALID_ARG;
+    if (mode >= 1 && (!src || span < 32768 || span % 16 != 0)) return MOE_ERR_INVALID_ARG;
+    if (!sink) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_calibrate_kstep(src, (long)span, workgroups, steps, mode, sink, stream));
+}
+
 }  // extern "C"
