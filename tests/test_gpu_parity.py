@@ -129,6 +129,10 @@ SMALL = [
     # large-tile (direct-to-LDS) path: K % 64 == 0, >= 96 rows per expert, partial N tiles
     ("tiny", {"T": 700, "H": 128, "F": 192, "E": 5, "k": 2, "dtype": "bf16", "seed": 87}),
     ("tiny", {"T": 300, "H": 256, "F": 320, "E": 4, "k": 2, "dtype": "bf16", "seed": 88, "Fs": 192}),
+    # Fs == F on the large tiles: the shared expert is one more group of the routed launches (ragged last
+    # shared M-tile, partial N tile; with drop)
+    ("tiny", {"T": 300, "H": 256, "F": 320, "E": 4, "k": 2, "dtype": "bf16", "seed": 90, "Fs": 320}),
+    ("tiny", {"T": 520, "H": 128, "F": 256, "E": 3, "k": 2, "dtype": "bf16", "seed": 91, "Fs": 256, "drop": 0.2}),
     ("tiny", {"T": 1100, "H": 192, "F": 128, "E": 8, "k": 3, "dtype": "bf16", "seed": 89, "drop": 0.2,
               "zipf": 1.2}),
 ]

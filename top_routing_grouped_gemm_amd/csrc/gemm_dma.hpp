@@ -95,9 +95,12 @@ __device__ __forceinline__ int swz_b(int row, int chunk) { return chunk ^ (2 * (
 // Map this workgroup to (expert, M-tile rows, N-tile). All waves compute the
 // same answer; returns false for workgroups past the last tile. Only groups
 // with rmin <= rows < rmax get tiles (another launch takes the others).
+// extra_rows > 0 (with offsets only): one more group of that many rows after
+// the E groups, reported as e_out == E with rows [0, extra_rows) of its own.
 template <int BM>
-__device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, int E, int fixed_rows, int n_tiles,
-                                         int rmin, int rmax, int& e_out, int& rb, int& re, int& nt) {
+__device__ __forceinline__ bool xcd_tile_lanes(const int32_t* __restrict__ offsets, int E, int fixed_rows,
+                                               int n_tiles, int rmin, int rmax, int& e_out, int& rb, int& re, int& nt,
+                                               int extra_rows) {
     const int l = lane_id();
     int total_m, incl = 0, s = 0, per = 1;
     if (offsets == nullptr) {
@@ -112,6 +115,8 @@ __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, in
         incl = wave_incl_scan(s);
         total_m = __shfl(incl, kWave - 1, kWave);
     }
+    const int grouped_m = total_m;
+    total_m += (extra_rows + BM - 1) / BM;
     const long total = (long)total_m * n_tiles;
     const long chunk = (total + kXcds - 1) / kXcds;
     const long b = blockIdx.x;
@@ -124,6 +129,12 @@ __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, in
         e_out = 0;
         rb = mt * BM;
         re = min(fixed_rows, rb + BM);
+        return true;
+    }
+    if (mt >= grouped_m) {
+        e_out = E;
+        rb = (mt - grouped_m) * BM;
+        re = min(extra_rows, rb + BM);
         return true;
     }
     const unsigned long long own = __ballot(mt < incl);
@@ -141,6 +152,22 @@ __device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, in
     rb = offsets[e] + (mt - before) * BM;
     re = min(offsets[e + 1], rb + BM);
     return true;
+}
+
+// The tile is the same for every lane; saying so keeps it, and the pointers
+// and buffer descriptors derived from it, in scalar registers (otherwise each
+// epilogue buffer store is wrapped in a loop over distinct descriptor values).
+template <int BM>
+__device__ __forceinline__ bool xcd_tile(const int32_t* __restrict__ offsets, int E, int fixed_rows, int n_tiles,
+                                         int rmin, int rmax, int& e_out, int& rb, int& re, int& nt,
+                                         int extra_rows = 0) {
+    e_out = rb = re = nt = 0;
+    const bool ok = xcd_tile_lanes<BM>(offsets, E, fixed_rows, n_tiles, rmin, rmax, e_out, rb, re, nt, extra_rows);
+    e_out = __builtin_amdgcn_readfirstlane(e_out);
+    rb = __builtin_amdgcn_readfirstlane(rb);
+    re = __builtin_amdgcn_readfirstlane(re);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    return __builtin_amdgcn_readfirstlane((int)ok) != 0;
 }
 
 // C[rows of group e, n-tile] = A[rows] @ B_e with the fused epilogue, on
@@ -363,6 +390,18 @@ struct Tile32 {
     static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
+// One more group of a grouped launch with operands of its own: the shared
+// expert (every token, read from x directly, its own weight matrix and
+// output). rows == 0: none. Its tiles follow the E groups' tiles.
+struct ExtraGroup {
+    const uint16_t* A;  // A of its rows 0..rows-1, same conventions as the kernel's A
+    long lda, a_kstep;
+    const void* B;      // one weight matrix (no expert stride)
+    void* C;            // its output, same conventions as the kernel's C
+    long ldc, c_cap;
+    int rows;
+};
+
 // a_rows (nullable): A row of output row r is a_rows[r] (the permute folded
 // into the A-tile loads: A is then x[T,H] and a_rows the row -> token map).
 // A element (r, k) sits at A[r*lda + (k/BK)*BK*a_kstep + k%BK]: row-major is
@@ -374,7 +413,8 @@ struct Tile32 {
 // expert e, applied to the fp32 accumulators before the epilogue. The codes
 // widen exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1), so the MFMAs
 // are the bf16 ones and sum_k a*code is exact up to fp32 accumulation.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool F8B = false>
+// xg: the extra group (bf16 B only), stored with epilogue EPI2.
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool F8B = false, int EPI2 = EPI>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t* __restrict__ A, long lda,
                                                                  long a_kstep, const int32_t* __restrict__ a_rows,
                                                                  const void* __restrict__ B, long strideB, long ldb,
@@ -382,16 +422,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
                                                                  void* __restrict__ C, long ldc, long c_cap,
                                                                  const int32_t* __restrict__ offsets, int E,
                                                                  int fixed_rows, int rmin, int rmax, int N, int K,
-                                                                 int n_tiles) {
+                                                                 int n_tiles, ExtraGroup xg) {
     using Tl = Tile32<BM, BN, BK, NS, WM, WN, F8B>;
     constexpr int NW = Tl::NW, TM = Tl::TM, TN = Tl::TN, WTM = Tl::WTM, WTN = Tl::WTN;
     constexpr int A_BYTES = Tl::A_BYTES, STAGE = Tl::STAGE, LOADS = Tl::LOADS;
     __shared__ __align__(1024) uint8_t smem[NS * STAGE];
 
     int e, rb, re, nt;
-    if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, rmin, rmax, e, rb, re, nt)) return;
+    if (!xcd_tile<BM>(offsets, E, fixed_rows, n_tiles, rmin, rmax, e, rb, re, nt, F8B ? 0 : xg.rows)) return;
     const int n0 = nt * BN;
-    const uint8_t* Be = (const uint8_t*)B + (long)e * strideB * (F8B ? 1 : 2);
+    const bool extra = !F8B && e == E;
+    if (extra) {
+        A = xg.A;
+        lda = xg.lda;
+        a_kstep = xg.a_kstep;
+        a_rows = nullptr;
+        C = xg.C;
+        ldc = xg.ldc;
+        c_cap = xg.c_cap;
+    }
+    const uint8_t* Be = extra ? (const uint8_t*)xg.B : (const uint8_t*)B + (long)e * strideB * (F8B ? 1 : 2);
     const int wave = threadIdx.x / kWave, l = lane_id();
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
 
@@ -552,6 +602,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
 
     // the epilogue's buffer ranges span this tile's rows only (re - rb can exceed 2^31 bytes of C for one
     // very large group)
+    if constexpr (EPI2 != EPI) {
+        if (extra) {
+            store_tile32<TM, TN, WTM, WTN, EPI2>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
+            return;
+        }
+    }
     store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
 }
 

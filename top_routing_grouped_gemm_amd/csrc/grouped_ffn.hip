@@ -261,17 +261,21 @@ using DmaStream = DmaCfg<32, 128, 64, 4, 1, 4>;
 
 // a_kstep / c_cap: see gemm32_kernel (1 / 0 for row-major A / C).
 // [rmin, rmax): the group sizes this launch takes (see xcd_tile).
-template <class C, int EPI>
+// xg: one more group after the E groups (the shared expert), stored with EPI2.
+template <class C, int EPI, int EPI2 = EPI>
 hipError_t run_dma(const void* A, long lda, long a_kstep, const int32_t* a_rows, const void* B, long strideB, long ldb,
                    void* Cm, long ldc, long c_cap, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N,
-                   int K, hipStream_t s, int rmin = 0, int rmax = INT_MAX) {
+                   int K, hipStream_t s, int rmin = 0, int rmax = INT_MAX, dma::ExtraGroup xg = dma::ExtraGroup{}) {
     const int n_tiles = (N + C::BN - 1) / C::BN;
+    if (xg.rows > 0 && offsets == nullptr) return hipErrorInvalidValue;
     // XCD-chunked order needs up to kXcds-1 spare workgroups past the tile count
-    const long grid = max_mtiles(C::BM, offsets, E, fixed_rows, max_rows) * n_tiles + dma::kXcds;
+    const long grid =
+        (max_mtiles(C::BM, offsets, E, fixed_rows, max_rows) + (xg.rows + C::BM - 1) / C::BM) * n_tiles + dma::kXcds;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI>), dim3((unsigned)grid),
-                       dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_kstep, a_rows, B, strideB, ldb,
-                       nullptr, Cm, ldc, c_cap, offsets, E, fixed_rows, rmin, rmax, N, K, n_tiles);
+    hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI, false, EPI2>),
+                       dim3((unsigned)grid), dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, a_kstep, a_rows,
+                       B, strideB, ldb, nullptr, Cm, ldc, c_cap, offsets, E, fixed_rows, rmin, rmax, N, K, n_tiles,
+                       xg);
     return hipGetLastError();
 }
 
@@ -293,7 +297,8 @@ hipError_t run_dma8(const void* A, long lda, const int32_t* a_rows, const void* 
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dma::gemm32_kernel<C::BM, C::BN, C::BK, C::NS, C::WM, C::WN, EPI, true>),
                        dim3((unsigned)grid), dim3(C::WM * C::WN * 64), 0, s, (const uint16_t*)A, lda, 1L, a_rows, Bq,
-                       strideB, 0L, bscale, Cm, ldc, c_cap, offsets, E, 0, rmin, rmax, N, K, n_tiles);
+                       strideB, 0L, bscale, Cm, ldc, c_cap, offsets, E, 0, rmin, rmax, N, K, n_tiles,
+                       dma::ExtraGroup{});
     return hipGetLastError();
 }
 
@@ -383,22 +388,24 @@ bool dma_ok(long lda, long ldb, int N, int K) {
 
 // h_cap > 0: the k-blocked h layout (W1 writes it as C, W2 reads it as A);
 // only the large direct-to-LDS shape takes it (h_blocked decides).
+// xg (large-tile shape only, see ffn_shared_merges): the shared expert's group.
 template <int EPI>
 hipError_t run_bf16_cfg(TileCfg cfg, const void* A, long lda, const void* B, long strideB, long ldb, void* C,
                         long ldc, const int32_t* offsets, int E, int fixed_rows, int max_rows, int N, int K,
-                        long h_cap, hipStream_t s) {
+                        long h_cap, hipStream_t s, dma::ExtraGroup xg = dma::ExtraGroup{}) {
     if (h_cap > 0) {
         if (EPI == kEpiSiluOut)  // W1: C = h blocked
             return run_dma<DmaLarge, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, h_cap, offsets, E, fixed_rows,
-                                          max_rows, N, K, s);
+                                          max_rows, N, K, s, 0, INT_MAX, xg);
         return run_dma<DmaLarge, EPI>(A, 32, h_cap, nullptr, B, strideB, ldb, C, ldc, 0, offsets, E, fixed_rows,
-                                      max_rows, N, K, s);  // W2: A = h blocked
+                                      max_rows, N, K, s, 0, INT_MAX, xg);  // W2: A = h blocked
     }
+    if (xg.rows > 0 && (cfg != kTileM128 || !dma_ok<DmaLarge>(lda, ldb, N, K))) return hipErrorInvalidValue;
     switch (cfg) {
         case kTileM128:
             if (dma_ok<DmaLarge>(lda, ldb, N, K))
                 return run_dma<DmaLarge, EPI>(A, lda, 1, nullptr, B, strideB, ldb, C, ldc, 0, offsets, E, fixed_rows,
-                                              max_rows, N, K, s);
+                                              max_rows, N, K, s, 0, INT_MAX, xg);
             return run_bf16<128, 128, 64, 2, 2, EPI>(A, lda, B, strideB, ldb, C, ldc, offsets, E, fixed_rows,
                                                      max_rows, N, K, s);
         case kTileMixed:
@@ -445,11 +452,32 @@ bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt) {
     return false;
 }
 
+bool ffn_shared_merges(TileCfg cfg, int H, int F, int Fs, Dtype dt) {
+    return dt == kBF16 && Fs == F && cfg == kTileM128 && dma_ok<DmaLarge>(H, F, F, H) && dma_ok<DmaLarge>(F, H, H, F);
+}
+
+namespace {
+// The shared expert as the W1 / W2 launch's extra group (row-major x; its h
+// k-blocked when sh.h_cap > 0, like the routed h).
+dma::ExtraGroup shared_up(const SharedGroup* sh, int H, int F) {
+    if (sh == nullptr) return dma::ExtraGroup{};
+    return dma::ExtraGroup{(const uint16_t*)sh->x, H, 1, sh->W1s, sh->h, F, sh->h_cap, sh->T};
+}
+dma::ExtraGroup shared_down(const SharedGroup* sh, int F, int H) {
+    if (sh == nullptr) return dma::ExtraGroup{};
+    const bool blk = sh->h_cap > 0;
+    return dma::ExtraGroup{(const uint16_t*)sh->h, blk ? 32L : (long)F, blk ? sh->h_cap : 1L, sh->W2s, sh->y, H, 0,
+                           sh->T};
+}
+}  // namespace
+
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                                const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s) {
+                                const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s,
+                                const SharedGroup* sh) {
+    if (sh != nullptr && cfg != kTileM128) return hipErrorInvalidValue;
     if (cfg == kTileM128)
         return run_dma<DmaLarge, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, h_cap, offsets, E, 0,
-                                              max_rows, F, H, s);
+                                              max_rows, F, H, s, 0, INT_MAX, shared_up(sh, H, F));
     if (cfg == kTileMixed) {
         const hipError_t e = run_dma<DmaStream, kEpiSiluOut>(x, H, 1, row_token, W1, (long)H * F, F, h, F, 0, offsets,
                                                              E, 0, max_rows, F, H, s, 0, kStreamRows);
@@ -477,14 +505,18 @@ bool ffn_down_packs(TileCfg cfg, int F, int H, Dtype dt) {
 }
 
 hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, int max_rows, const void* W2, int F,
-                                  int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s) {
+                                  int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s,
+                                  const SharedGroup* sh) {
     const long sb = (long)F * H;
+    if (sh != nullptr && cfg != kTileM128) return hipErrorInvalidValue;
     if (cfg == kTileM128) {
+        // the shared expert's rows go to fp32 y_shared (EPI2), the routed rows to the packed planes
         if (h_cap > 0)
-            return run_dma<DmaLarge, kEpiScaled16>(h, 32, h_cap, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0,
-                                                   max_rows, H, F, s);
-        return run_dma<DmaLarge, kEpiScaled16>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E, 0, max_rows,
-                                               H, F, s);
+            return run_dma<DmaLarge, kEpiScaled16, kEpiF32Out>(h, 32, h_cap, nullptr, W2, sb, H, y_planes, H, cap,
+                                                               offsets, E, 0, max_rows, H, F, s, 0, INT_MAX,
+                                                               shared_down(sh, F, H));
+        return run_dma<DmaLarge, kEpiScaled16, kEpiF32Out>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets, E,
+                                                           0, max_rows, H, F, s, 0, INT_MAX, shared_down(sh, F, H));
     }
     if (cfg == kTileMixed) {
         const hipError_t e = run_dma<DmaStream, kEpiScaled16>(h, F, 1, nullptr, W2, sb, H, y_planes, H, cap, offsets,
@@ -547,20 +579,24 @@ TileCfg choose_tile(long rows, int groups) {
 }
 
 hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed_rows, int max_rows, const void* W1,
-                         int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s) {
+                         int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s,
+                         const SharedGroup* sh) {
     const long strideB = (offsets == nullptr) ? 0 : (long)H * F;
+    if (sh != nullptr && (dt != kBF16 || offsets == nullptr)) return hipErrorInvalidValue;
     if (dt == kBF16)
         return run_bf16_cfg<kEpiSiluOut>(cfg, A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H,
-                                         h_cap, s);
+                                         h_cap, s, shared_up(sh, H, F));
     return run_f32<kEpiSiluOut>(A, H, W1, strideB, F, h, F, offsets, E, fixed_rows, max_rows, F, H, s);
 }
 
 hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
-                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s) {
+                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s,
+                           const SharedGroup* sh) {
     const long strideB = (offsets == nullptr) ? 0 : (long)F * H;
+    if (sh != nullptr && (dt != kBF16 || offsets == nullptr)) return hipErrorInvalidValue;
     if (dt == kBF16)
         return run_bf16_cfg<kEpiF32Out>(cfg, h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, h_cap,
-                                        s);
+                                        s, shared_down(sh, F, H));
     return run_f32<kEpiF32Out>(h, F, W2, strideB, H, y, H, offsets, E, fixed_rows, max_rows, H, F, s);
 }
 

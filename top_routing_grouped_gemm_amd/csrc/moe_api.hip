@@ -169,20 +169,26 @@ int enqueue_ffn(const void* x_perm, const int32_t* row_token, const int32_t* off
     const int rows = T * k;
     const moe::TileCfg cfg = moe::choose_tile(rows, E);
     const long hc = moe::h_blocked(cfg, H, F, rows, d);  // h layout shared by the W1 and W2 launches
-    // shared expert: one fixed group of T rows reading x directly
+    // shared expert: every token, read from x directly. Where the routed launches' tile shape allows it
+    // (page 3, "MoE层的结构与token路由": the shared expert sees every token besides the routed ones), it is one
+    // more group of T rows in the same two launches; otherwise two launches of its own.
     void* hs = base + L.h_sh;
-    const moe::TileCfg cs = moe::choose_tile(T, 1);
+    const bool merged = W1s != nullptr && moe::ffn_shared_merges(cfg, H, F, Fs, d);
+    const moe::TileCfg cs = merged ? moe::kTileM128 : moe::choose_tile(T, 1);
     const long hsc = W1s != nullptr ? moe::h_blocked(cs, H, Fs, T, d) : 0;
+    const moe::SharedGroup sg{x, W1s, W2s, hs, hsc, y_shared, T};
+    const moe::SharedGroup* sh = merged ? &sg : nullptr;
     if (row_token != nullptr)
-        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, cfg, hc, h, s));
+        MOE_TRY(moe::launch_ffn_up_gather(x, row_token, offsets, E, rows, W1, H, F, cfg, hc, h, s, sh));
     else
-        MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, hc, s));
-    if (W1s != nullptr) MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, hsc, s));
+        MOE_TRY(moe::launch_ffn_up(x_perm, offsets, E, 0, rows, W1, H, F, d, h, cfg, hc, s, sh));
+    if (W1s != nullptr && !merged) MOE_TRY(moe::launch_ffn_up(x, nullptr, 1, T, T, W1s, H, Fs, d, hs, cs, hsc, s));
     if (packed)
-        MOE_TRY(moe::launch_ffn_down_packed(h, offsets, E, rows, W2, F, H, cfg, hc, y_perm, rows, s));
+        MOE_TRY(moe::launch_ffn_down_packed(h, offsets, E, rows, W2, F, H, cfg, hc, y_perm, rows, s, sh));
     else
-        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, hc, s));
-    if (W1s != nullptr) MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, hsc, s));
+        MOE_TRY(moe::launch_ffn_down(h, offsets, E, 0, rows, W2, F, H, d, y_perm, cfg, hc, s, sh));
+    if (W1s != nullptr && !merged)
+        MOE_TRY(moe::launch_ffn_down(hs, nullptr, 1, T, T, W2s, Fs, H, d, y_shared, cs, hsc, s));
     return MOE_OK;
 }
 

@@ -66,14 +66,32 @@ hipError_t launch_index(const int32_t* ids, const float* w, const int32_t* parti
 hipError_t launch_copy_rows(const void* x, const int32_t* inv, int T, int k, int row_bytes, void* x_perm,
                             hipStream_t s);
 
+// The shared expert as one more group of the routed launches: T rows of x
+// against W1s into its own h (h_cap as h_blocked gives for T rows, 0 for
+// row-major), then that h against W2s into fp32 y[T][H].
+struct SharedGroup {
+    const void *x, *W1s, *W2s;
+    void* h;
+    long h_cap;
+    float* y;
+    int T;
+};
+// Whether the routed launches of this tile shape can take the shared expert
+// as one more group: bf16, Fs == F, the large direct-to-LDS tiles.
+bool ffn_shared_merges(TileCfg cfg, int H, int F, int Fs, Dtype dt);
+
 // Grouped FFN. Rows of group e are [offsets[e], offsets[e+1]); with offsets == NULL there
-// is a single group of rows [0, fixed_rows) (the shared expert).
+// is a single group of rows [0, fixed_rows) (the shared expert on its own).
 // h_cap: 0 for a row-major h[rows, F]; > 0 (from h_blocked) for the k-blocked
 // h[F/32][h_cap][32] that the W1 launch writes and the W2 launch reads.
+// sh (nullable; offsets != NULL and ffn_shared_merges only): the shared expert
+// as one more group of the same launch.
 hipError_t launch_ffn_up(const void* A, const int32_t* offsets, int E, int fixed_rows, int max_rows,
-                         const void* W1, int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s);
+                         const void* W1, int H, int F, Dtype dt, void* h, TileCfg cfg, long h_cap, hipStream_t s,
+                         const SharedGroup* sh = nullptr);
 hipError_t launch_ffn_down(const void* h, const int32_t* offsets, int E, int fixed_rows, int max_rows,
-                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s);
+                           const void* W2, int F, int H, Dtype dt, float* y, TileCfg cfg, long h_cap, hipStream_t s,
+                           const SharedGroup* sh = nullptr);
 // W1 -> SiLU -> W2 in one launch with h kept in LDS (64-row tiles; bf16, F % 256 == 0, F <= 768,
 // H % 256 == 0): y_perm [max_rows][H] fp32.
 bool ffn_fused_ok(int H, int F, Dtype dt);
@@ -88,13 +106,15 @@ long h_blocked(TileCfg cfg, int H, int F, long cap, Dtype dt);
 // at ((int8_t*)planes + cap*H*2)[r*(H/32) + n/32]; cap*H*(2 + 1/32) bytes.
 bool ffn_down_packs(TileCfg cfg, int F, int H, Dtype dt);
 hipError_t launch_ffn_down_packed(const void* h, const int32_t* offsets, int E, int max_rows, const void* W2, int F,
-                                  int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s);
+                                  int H, TileCfg cfg, long h_cap, void* y_planes, long cap, hipStream_t s,
+                                  const SharedGroup* sh = nullptr);
 TileCfg choose_tile(long rows, int groups);
 // Whether the W1 launch for this tile shape can read token rows of x directly
 // through the row -> token map (the permute copy is then not needed).
 bool ffn_up_gathers(TileCfg cfg, int H, int F, Dtype dt);
 hipError_t launch_ffn_up_gather(const void* x, const int32_t* row_token, const int32_t* offsets, int E, int max_rows,
-                                const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s);
+                                const void* W1, int H, int F, TileCfg cfg, long h_cap, void* h, hipStream_t s,
+                                const SharedGroup* sh = nullptr);
 
 // fp8 expert weights (fp8_quant.hip): bytes of the tiled codes of E matrices
 // [K][N], and the quantiser (scales[E][N] fp32, codes in the tiled layout).
