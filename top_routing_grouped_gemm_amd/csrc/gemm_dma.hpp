@@ -364,6 +364,113 @@ __device__ __forceinline__ void store_tile32(f32x16 (&acc)[TM][TN], void* C, lon
         }
 }
 
+// The same stores for accumulators of the swapped product: with the weight
+// fragment as the MFMA's first operand and the activation fragment as its
+// second, block (i, j) holds the transposed 32x32 result, so lane l owns row
+// wm*WTM + i*32 + l%32 and, in acc[i][j][4p..4p+3], the 4 adjacent columns
+// wn*WTN + j*32 + 8p + 4*(l/32) + 0..3. No cross-lane transpose is needed, and
+// the 32 columns of a row's block sit in lanes l and l^32 (EPI 4's block
+// maximum is 15 local maxima and one permlane32 swap). Same layouts, ranges
+// and dropped stores as store_tile32.
+template <int TM, int TN, int WTM, int WTN, int EPI>
+__device__ __forceinline__ void store_tile32s(f32x16 (&acc)[TM][TN], void* C, long ldc, long c_cap, int rb, int re,
+                                              int n0, int N, int wm, int wn) {
+    const int l = lane_id();
+    const int h4 = 4 * (l >> 5);
+    if constexpr (EPI == 4) {
+        const int lds = (int)(ldc / 32);  // scale bytes per row
+        const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+            (uint8_t*)C + ((long)rb * ldc + n0) * 2, (short)0, (int)(((long)(re - rb) * ldc - n0) * 2), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+            (uint8_t*)C + c_cap * ldc * 2 + (long)rb * lds + n0 / 32, (short)0, (int)((long)(re - rb) * lds - n0 / 32),
+            0x00020000);
+        constexpr bool kWord = TN % 4 == 0;
+        const bool word = kWord && ldc % 128 == 0 && n0 % 128 == 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int rowrel = wm * WTM + i * 32 + (l & 31);
+            uint32_t sw = 0;
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj) {
+                const int blk = wn * WTN + jj * 32;  // first column of this 32-column block, tile-relative
+                const bool col_ok = n0 + blk < N;    // N % 32 == 0: whole blocks
+                int b = 0;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) b = max(b, __float_as_int(acc[i][jj][q]) & 0x7fffffff);
+                const auto sx = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
+                b = col_ok ? max((int)sx[0], (int)sx[1]) : 0;
+                const float am = __int_as_float(b);
+                const int ex = (int)((__float_as_uint(am) >> 23) & 0xffu);
+                const int sc = am > 0.0f ? min(127, max(-127, ex - 127 - 14)) : 0;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t hbits[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const _Float16 h = (_Float16)ldexpf(acc[i][jj][4 * p + q], -sc);
+                        hbits[q] = (uint32_t)__builtin_bit_cast(uint16_t, h);
+                    }
+                    typedef __attribute__((ext_vector_type(2))) unsigned u2;
+                    const u2 pk = {hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16)};
+                    const int e = rowrel * (int)ldc + blk + 8 * p + h4;  // element offset within the tile's rows
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, rs_v, col_ok ? e * 2 : 0x7ffffff0, 0, 0);
+                }
+                // the row's scale byte: lane l < 32 (lane l + 32 holds the other half of the same row)
+                if (kWord) sw |= (uint32_t)(uint8_t)(int8_t)sc << (8 * (jj & 3));
+                if (!word)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)sc, rs_s,
+                                                         (col_ok && l < 32) ? rowrel * lds + blk / 32 : 0x7ffffff0, 0,
+                                                         0);
+                if (kWord && (jj & 3) == 3) {
+                    const int blk0 = blk - 96;  // the group's first block
+                    if (word)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            sw, rs_s, (l < 32 && n0 + blk0 < N) ? rowrel * lds + blk0 / 32 : 0x7ffffff0, 0, 0);
+                    sw = 0;
+                }
+            }
+        }
+        return;
+    }
+    constexpr int ES = EPI == 0 ? 2 : 4;
+    const long ldc_b = ldc * ES;
+    const bool blocked = c_cap > 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        blocked ? __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)((long)N * c_cap * ES), 0x00020000)
+                : __builtin_amdgcn_make_buffer_rsrc((uint8_t*)C + (long)rb * ldc_b + (long)n0 * ES, (short)0,
+                                                    (int)((long)(re - rb) * ldc_b - (long)n0 * ES), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int rowrel = wm * WTM + i * 32 + (l & 31);
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int colrel = wn * WTN + jj * 32 + 8 * p + h4;
+                const bool col_ok = n0 + colrel < N;  // N % 8 == 0: all 4 columns or none
+                int off;
+                if (blocked)
+                    off = (col_ok && rowrel < re - rb)
+                              ? (int)((((long)(n0 + colrel) >> 5) * c_cap + rb + rowrel) * (32 * ES) +
+                                      ((n0 + colrel) & 31) * ES)
+                              : 0x7ffffff0;
+                else
+                    off = col_ok ? rowrel * (int)ldc_b + colrel * ES : 0x7ffffff0;
+                const float v[4] = {acc[i][jj][4 * p], acc[i][jj][4 * p + 1], acc[i][jj][4 * p + 2],
+                                    acc[i][jj][4 * p + 3]};
+                if (EPI == 0) {
+                    typedef __attribute__((ext_vector_type(2))) unsigned u2;
+                    const u2 pk = {pack_bf16x2(silu_f32(v[0]), silu_f32(v[1])),
+                                   pack_bf16x2(silu_f32(v[2]), silu_f32(v[3]))};
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, rsrc, off, 0, 0);
+                } else {
+                    const f32x4 pk = {v[0], v[1], v[2], v[3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(pk, rsrc, off, 0, 0);
+                }
+            }
+    }
+}
+
 // fp8 B operand (F8B): expert weights as OCP e4m3 codes in 8 KiB tiles of
 // 128 output columns x 64 k, laid out [N/128][K/64][128 n][64 k] per expert,
 // with the 8-byte k-chunk c of column n stored at chunk c ^ f8_swz(n). A
@@ -414,6 +521,10 @@ struct ExtraGroup {
 // widen exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1), so the MFMAs
 // are the bf16 ones and sum_k a*code is exact up to fp32 accumulation.
 // xg: the extra group (bf16 B only), stored with epilogue EPI2.
+// With bf16 B the weight fragment is the MFMA's first operand and the results
+// are stored by store_tile32s (no transpose; measured 1-2 % faster per launch
+// at prefill, bit-identical results); the fp8 path keeps the activation first,
+// so each lane's accumulators share one column and one weight scale.
 template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool F8B = false, int EPI2 = EPI>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t* __restrict__ A, long lda,
                                                                  long a_kstep, const int32_t* __restrict__ a_rows,
@@ -426,6 +537,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     using Tl = Tile32<BM, BN, BK, NS, WM, WN, F8B>;
     constexpr int NW = Tl::NW, TM = Tl::TM, TN = Tl::TN, WTM = Tl::WTM, WTN = Tl::WTN;
     constexpr int A_BYTES = Tl::A_BYTES, STAGE = Tl::STAGE, LOADS = Tl::LOADS;
+    constexpr bool SWP = !F8B;
     __shared__ __align__(1024) uint8_t smem[NS * STAGE];
 
     int e, rb, re, nt;
@@ -552,7 +664,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = SWP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0)
+                                : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
     // Fragments of k-slice j are read while the MFMAs of slice j-1 run. The
     // last slice of a stage is multiplied only after the next barrier, so the
@@ -604,11 +717,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm32_kernel(const uint16_t*
     // very large group)
     if constexpr (EPI2 != EPI) {
         if (extra) {
-            store_tile32<TM, TN, WTM, WTN, EPI2>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
+            if constexpr (SWP) store_tile32s<TM, TN, WTM, WTN, EPI2>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
+            else store_tile32<TM, TN, WTM, WTN, EPI2>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
             return;
         }
     }
-    store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
+    if constexpr (SWP) store_tile32s<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
+    else store_tile32<TM, TN, WTM, WTN, EPI>(acc, C, ldc, c_cap, rb, min(re, rb + BM), n0, N, wm, wn);
 }
 
 }  // namespace dma

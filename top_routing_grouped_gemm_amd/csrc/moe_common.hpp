@@ -23,9 +23,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Pack two floats into a bf16x2 word (lo = a, hi = b), RNE.
+// Pack two floats into a bf16x2 word (lo = a, hi = b), RNE: one v_cvt_pk_bf16_f32 on gfx950, the same bits
+// as f32_to_bf16_bits for finite values.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
