@@ -486,7 +486,20 @@ def cpu_baseline(I_name, min_seconds=10.0, max_reps=30):
             stage[k_] = stage.get(k_, 0.0) + v
     return {"value": round(reps * I.T / total, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{reps} x the whole {I_name} batch (T={I.T} tokens), fp64 numpy/OpenBLAS, {total:.1f} s",
+            "cpu": host_cpu_model(),
             "stages_s": {k_: round(v / reps, 3) for k_, v in stage.items()}}
+
+
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None where it is not readable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def calibration():
