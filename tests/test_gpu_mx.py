@@ -245,11 +245,10 @@ def test_mx_layer_small(dev, over):
     _say(f"  h codes at a rounding boundary: {flips} of {n}; y max-abs/rms {rel:.3e}")
 
 
-@pytest.mark.parametrize("name,nsample", [("prefill", 6), ("decode", 6)])
-def test_mx_full_workload(dev, name, nsample):
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_mx_full_workload(dev, name):
+    """Full-size MX layer, every token: h codes and scales, y_perm rows and y against the oracle."""
     I = gen.make_inputs(name)
     _say(f"mx full {name}: T={I.T} H={I.H} F={I.F} E={I.E} k={I.k}")
-    rng = np.random.default_rng(10)
-    toks = np.array(sorted(set(rng.choice(I.T, size=nsample, replace=False).tolist()) | {0, I.T - 1}))
-    flips, n, rel = _validate_layer(dev, I, toks)
-    _say(f"  {name}: h codes at a rounding boundary: {flips} of {n}; y max-abs/rms {rel:.3e} on {len(toks)} tokens")
+    flips, n, rel = _validate_layer(dev, I)
+    _say(f"  {name}: h codes at a rounding boundary: {flips} of {n}; y max-abs/rms {rel:.3e} on all {I.T} tokens")
