@@ -46,7 +46,26 @@ def _draw_configs(n=20, seed=2024):
     return out
 
 
-CONFIGS = _draw_configs(40)
+def _draw_shared_merged(n=8, seed=2025):
+    """bf16 layers whose shared expert runs as one more group of the routed launches: Fs == F, enough rows per
+    expert for the large tiles (T*k/E >= 96), K and N multiples of 32, ragged T and F."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 4, 8]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        T = int(rng.choice([300, 513, 700, 1000, 2000]))
+        if T * k // E < 96:
+            T = 96 * E // k + 37
+        H = int(32 * rng.integers(2, 17))
+        F = int(32 * rng.integers(2, 21))
+        drop = float(rng.choice([0.0, 0.1])) if k > 1 else 0.0
+        out.append(dict(T=T, H=H, F=F, E=E, k=k, drop=min(drop, 1.0 / k), zipf=0.0, Fs=F, dtype="bf16",
+                        seed=3100 + i))
+    return out
+
+
+CONFIGS = _draw_configs(40) + _draw_shared_merged(8)
 
 
 def _check_y(y_gpu, y_ref, tol=Y_TOL):
