@@ -8,8 +8,8 @@ rate on the same FLOPs beside it), per-stage times with and without the MALL
 evicted and their HBM fractions, the grouped FFN with h kept on chip beside
 the two-launch one, the decode-shaped layer (T=32; weight stream, graph
 replay, fp8 and MX fp8 experts), the Mixtral-like layer with a shared expert
-and the skewed-routing layer, ceilings measured on the box (bare MFMA loop,
-streaming read, a large library GEMM), and the fp64 CPU oracle timed on the
+and the skewed-routing layer, ceilings measured on the same GPU (bare MFMA loop,
+streaming read, the GEMM k-step, a large library GEMM), and the fp64 CPU oracle timed on the
 host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
