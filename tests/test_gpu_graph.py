@@ -22,6 +22,7 @@ CASES = [
     ("decode-bf16", dict(T=32, H=256, F=256, E=16, k=4, seed=701), "bf16"),   # weight-streaming tiles
     ("prefill-bf16", dict(T=600, H=256, F=256, E=4, k=2, seed=702), "bf16"),  # 256x256 tiles, k-blocked h
     ("drop-shared", dict(T=64, H=128, F=128, E=8, k=2, seed=703, drop=0.2, Fs=64), "bf16"),
+    ("shared-in-routed-launches", dict(T=600, H=256, F=256, E=4, k=2, seed=707, Fs=256), "bf16"),  # Fs == F
     ("decode-fp8", dict(T=32, H=256, F=256, E=16, k=4, seed=704), "fp8"),
     ("prefill-mx", dict(T=600, H=256, F=256, E=4, k=2, seed=705), "mx"),
     ("large-batch", dict(T=4096, H=256, F=256, E=64, k=4, seed=706), "bf16"),  # 64-token router workgroups,
