@@ -45,6 +45,8 @@ def _both(d, I, dev):
     ("decode", {"T": 5, "H": 256, "F": 128, "E": 16, "k": 4}),        # smaller, right after
     ("tiny", {"T": 300, "H": 256, "F": 256, "E": 12, "k": 3, "dtype": "bf16", "Fs": 128, "drop": 0.2,
               "zipf": 1.2}),                                          # mixed regimes, shared expert, drop
+    ("tiny", {"T": 600, "H": 256, "F": 256, "E": 4, "k": 2, "dtype": "bf16", "Fs": 256}),  # shared expert in the
+                                                                                            # routed launches
 ])
 def test_noalloc_matches_forward(dev, name, over):
     I = gen.make_inputs(name, **over)
