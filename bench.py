@@ -504,19 +504,23 @@ def host_cpu_model():
 
 def calibration():
     """Practical ceilings on this machine, measured with the library's calibration kernels: the bare bf16 MFMA loop
-    with one and two waves per SIMD (256 workgroups of 4 / 8 waves), and a streaming read of 2 GiB."""
+    with one and two waves per SIMD (256 workgroups of 4 / 8 waves) on one fixed operand pair, and with two waves
+    per SIMD on pseudo-random operands (what a GEMM on real data can reach: the matrix cores switch more bits and
+    run slower); a streaming read of 2 GiB; the grouped FFN's k-step on random bf16 operands with and without its
+    feed; the vendor library's 8192^3 bf16 GEMM on normal random operands."""
     import torch
 
     import top_routing_grouped_gemm_amd as moe
 
     s = torch.cuda.current_stream()
     out = {}
-    for waves in (4, 8):
+    for waves, rnd in ((4, False), (8, False), (8, True)):
         iters = 4096
         sink = torch.empty(256 * waves * 64, dtype=torch.float32, device="cuda")
-        flops = moe.moe_calibrate_mfma_bf16(256, waves, iters, sink)
-        ms = event_time_ms(lambda: moe.moe_calibrate_mfma_bf16(256, waves, iters, sink), 5, s)
-        out[f"mfma_32x32x16_bf16_{waves // 4}_wave_per_simd_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        flops = moe.moe_calibrate_mfma_bf16(256, waves, iters, sink, random_operands=rnd)
+        ms = event_time_ms(lambda: moe.moe_calibrate_mfma_bf16(256, waves, iters, sink, random_operands=rnd), 5, s)
+        key = f"mfma_32x32x16_bf16_{waves // 4}_wave_per_simd" + ("_random_operands" if rnd else "")
+        out[key + "_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     for wg in (1024, 4096):
         sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
@@ -525,8 +529,9 @@ def calibration():
         out[f"stream_read_{wg}_workgroups_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     del buf
     # the grouped FFN's 256x256 k-step alone, with its 32 KB-per-step direct-to-LDS feed from an L2-resident
-    # 4 MiB span, and that feed alone: the main loop's own ceiling with and without the feed
-    src = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+    # 4 MiB span of normal random bf16, and that feed alone: the main loop's own ceiling with and without the feed
+    # (mode 0 fills its LDS with pseudo-random bf16 itself)
+    src = torch.randn(2 << 20, device="cuda").to(torch.bfloat16).view(torch.uint8)
     sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
     steps = 512
     ks = {}

@@ -452,9 +452,12 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
  * moe_calibrate_mfma_bf16: `workgroups` workgroups of `waves_per_workgroup`
  *   (1..8) waves; each wave issues iters x 8 independent
  *   v_mfma_f32_32x32x16_bf16 and nothing else, i.e.
- *   workgroups * waves_per_workgroup * iters * 8 * 32768 FLOP. One float per
- *   thread goes to sink[workgroups * waves_per_workgroup * 64] (keeps the
- *   loop from being removed; the values mean nothing).
+ *   workgroups * waves_per_workgroup * iters * 8 * 32768 FLOP. operands 0:
+ *   one fixed low-entropy operand pair for every MFMA; 1: each of the 8
+ *   MFMAs its own pseudo-random bf16 operands (random signs and mantissas, as
+ *   a GEMM's fragments have), which switch more bits and run slower. One
+ *   float per thread goes to sink[workgroups * waves_per_workgroup * 64]
+ *   (keeps the loop from being removed; the values mean nothing).
  * moe_calibrate_stream_read: reads `bytes` (a multiple of 16) of `buf` once
  *   with 16-byte loads from `workgroups` workgroups of 256 threads, one float
  *   per thread to sink[workgroups * 256].
@@ -463,7 +466,8 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
  *   large tiles: 8 waves, a 4-stage ring of 32 KB stages, 16-byte and
  *   transpose LDS reads, 16 v_mfma_f32_32x32x16_bf16 per wave, one barrier),
  *   i.e. workgroups * steps * 4194304 FLOP, without the tile's epilogue.
- *   mode 0: on the LDS contents alone (src unused, may be NULL); mode 1: each
+ *   mode 0: on the LDS alone, filled once with pseudo-random bf16 (src
+ *   unused, may be NULL); mode 1: each
  *   step's stage also filled by 16-byte direct-to-LDS loads from src at byte
  *   offsets modulo span (span >= 32768, a multiple of 16; the whole span is
  *   read), 32 KB per step per workgroup; mode 2: those loads alone. One float
@@ -471,7 +475,8 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
  * All return MOE_ERR_INVALID_ARG for sizes outside these ranges or a null
  * pointer, MOE_ERR_HIP if the launch fails.
  */
-int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, float* sink, hipStream_t stream);
+int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, int operands, float* sink,
+                            hipStream_t stream);
 int moe_calibrate_stream_read(const void* buf, size_t bytes, int workgroups, float* sink, hipStream_t stream);
 int moe_calibrate_gemm_kstep(const void* src, size_t span, int workgroups, int steps, int mode, float* sink,
                              hipStream_t stream);

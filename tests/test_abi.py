@@ -362,6 +362,17 @@ def test_grouped_ffn_fused_limits(lib):
     assert call(T=0) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_calibrate_mfma_rejects(lib):
+    """The MFMA calibration aid refuses bad sizes and operand modes before any launch."""
+    N = None
+    assert lib.moe_calibrate_mfma_bf16(256, 8, 16, 2, _p(), N) == moe.MOE_ERR_INVALID_ARG    # operands 0 or 1
+    assert lib.moe_calibrate_mfma_bf16(256, 8, 16, -1, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calibrate_mfma_bf16(256, 9, 16, 0, _p(), N) == moe.MOE_ERR_INVALID_ARG    # 1..8 waves
+    assert lib.moe_calibrate_mfma_bf16(0, 8, 16, 1, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calibrate_mfma_bf16(256, 8, 0, 1, _p(), N) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calibrate_mfma_bf16(256, 8, 16, 1, N, N) == moe.MOE_ERR_INVALID_ARG      # no sink
+
+
 def test_calibrate_gemm_kstep_rejects(lib):
     """The k-step calibration aid refuses bad modes and feed spans before any launch."""
     N = None

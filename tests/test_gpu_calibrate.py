@@ -25,6 +25,9 @@ def test_calibration_kernels_run(dev):
             assert bool((sink == 0).all()), f"mode {mode}"
     sink2 = torch.empty(4 * 4 * 64, dtype=torch.float32, device=dev)
     assert moe.moe_calibrate_mfma_bf16(4, 4, 16, sink2) == 4 * 4 * 16 * 8 * 32768
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(sink2).all())
+    assert moe.moe_calibrate_mfma_bf16(4, 4, 16, sink2, random_operands=True) == 4 * 4 * 16 * 8 * 32768
     buf = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
     assert moe.moe_calibrate_stream_read(buf, 8) == 1 << 20
     torch.cuda.synchronize()

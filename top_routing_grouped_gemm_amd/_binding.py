@@ -118,7 +118,7 @@ def load_library(path: Optional[str] = None):
     lib.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
                                         vp, vp, vp, vp, vp]
     lib.moe_forward_noalloc.restype = i32
-    lib.moe_calibrate_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
+    lib.moe_calibrate_mfma_bf16.argtypes = [i32, i32, i32, i32, vp, vp]
     lib.moe_calibrate_mfma_bf16.restype = i32
     lib.moe_calibrate_stream_read.argtypes = [vp, sz, i32, vp, vp]
     lib.moe_calibrate_stream_read.restype = i32
@@ -663,11 +663,14 @@ def moe_grouped_ffn_mxfp8(x, row_token, expert_offsets, W1q, W1_scale, W2q, W2_s
     return h_codes, h_scale, y_perm
 
 
-def moe_calibrate_mfma_bf16(workgroups: int, waves: int, iters: int, sink=None, stream=None) -> int:
-    """Bare bf16 MFMA loop (measurement aid). Returns the FLOP count of the launch."""
+def moe_calibrate_mfma_bf16(workgroups: int, waves: int, iters: int, sink=None, stream=None,
+                            random_operands: bool = False) -> int:
+    """Bare bf16 MFMA loop (measurement aid), on one fixed operand pair or on pseudo-random operands per MFMA.
+    Returns the FLOP count of the launch."""
     sink = torch.empty(workgroups * waves * 64, dtype=torch.float32, device="cuda") if sink is None else sink
     _arg(sink, "sink", (workgroups * waves * 64,), torch.float32)
-    _check(load_library().moe_calibrate_mfma_bf16(workgroups, waves, iters, _ptr(sink), _stream(stream)),
+    _check(load_library().moe_calibrate_mfma_bf16(workgroups, waves, iters, int(bool(random_operands)), _ptr(sink),
+                                                  _stream(stream)),
            "moe_calibrate_mfma_bf16")
     return workgroups * waves * iters * 8 * 32768
 

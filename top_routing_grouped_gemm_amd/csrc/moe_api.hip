@@ -741,10 +741,11 @@ int moe_forward_mxfp8(const void* x, const void* Wr, const float* bias, const ui
         moe::launch_combine_packed(base + L.y, rows, iv, w, nullptr, T, H, k, (moe::Dtype)out_dt, y, stream));
 }
 
-int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, float* sink, hipStream_t stream) {
+int moe_calibrate_mfma_bf16(int workgroups, int waves_per_workgroup, int iters, int operands, float* sink,
+                            hipStream_t stream) {
     if (workgroups < 1 || waves_per_workgroup < 1 || waves_per_workgroup > 8 || iters < 1) return MOE_ERR_INVALID_ARG;
-    if (!sink) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_calibrate_mfma(workgroups, waves_per_workgroup, iters, sink, stream));
+    if (!sink || operands < 0 || operands > 1) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_calibrate_mfma(workgroups, waves_per_workgroup, iters, operands, sink, stream));
 }
 
 int moe_calibrate_stream_read(const void* buf, size_t bytes, int workgroups, float* sink, hipStream_t stream) {

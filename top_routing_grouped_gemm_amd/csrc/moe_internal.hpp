@@ -155,7 +155,7 @@ hipError_t launch_ffn_down_mx(const void* hq, const void* hs, long cap, const in
 hipError_t launch_combine_packed(const void* y_planes, long cap, const int32_t* inv, const float* w,
                                  const float* y_shared, int T, int H, int k, Dtype out_dt, void* y, hipStream_t s);
 // Measurement aids (calibrate.hip): a bare bf16 MFMA loop, a streaming read, the grouped FFN's k-step.
-hipError_t launch_calibrate_mfma(int workgroups, int waves, int iters, float* sink, hipStream_t s);
+hipError_t launch_calibrate_mfma(int workgroups, int waves, int iters, int operands, float* sink, hipStream_t s);
 hipError_t launch_calibrate_read(const void* buf, long bytes, int workgroups, float* sink, hipStream_t s);
 hipError_t launch_calibrate_kstep(const void* src, long span, int workgroups, int steps, int mode, float* sink,
                                   hipStream_t s);
