@@ -473,17 +473,18 @@ __device__ __forceinline__ void store_tile32s(f32x16 (&acc)[TM][TN], void* C, lo
 
 // The stores of store_tile32s through LDS, for a wave tile WTN = 128 columns
 // wide: the same values, layouts and dropped stores, but each store
-// instruction writes 1 KiB of whole lines (fp32 row-major: 2 rows x 512
-// bytes; SiLU + bf16 k-blocked: 16 consecutive rows x 64 bytes of one
-// 32-column block; block-scaled fp16: 4 rows x 256 bytes) instead of 16 or
-// 32 bytes on each of 16 or 32 lines, which a CU issues several times as
+// instruction writes whole lines (fp32 row-major: 2 rows x 512 bytes; SiLU +
+// bf16 k-blocked: 16 consecutive rows x 64 bytes of one 32-column block;
+// block-scaled fp16: 2 rows x 256 bytes) instead of 16 or 32 bytes on each
+// of 16 or 32 lines, which a CU issues several times as
 // fast: per-workgroup timestamps put the fp32 epilogue of a 256 x 256 tile at
 // 5.0 against 8.5-9.4 us. Launches gain less (about 1 % per layer), because
 // the faster stores now compete with the next tiles' loads.
 // Each wave stages its own 32 x 128 block (one i at a time) in its own LDS
 // region `st` (16 KiB) with the pieces of row r XOR-permuted by a function of
-// r, so the writes (32 rows at one column) and the reads (whole row pieces)
-// spread over the banks. The caller has made the region free (every wave past
+// r, so that in each pass of the LDS (128 bytes: 16 lanes of 8-byte or 8 of
+// 16-byte accesses) the writes (rows at one column) and the reads (pieces of
+// whole rows) touch distinct banks. The caller has made the region free (every wave past
 // the main loop's LDS reads). Supported: EPI 1 row-major, EPI 0 k-blocked,
 // EPI 4 (its scale bytes are stored directly, as in store_tile32s).
 template <int TM, int TN, int WTM, int WTN, int EPI>
@@ -523,7 +524,9 @@ __device__ __forceinline__ void store_tile32s_lds(f32x16 (&acc)[TM][TN], void* C
             }
         }
     } else if constexpr (EPI == 0) {
-        // k-blocked C: staged as [block j][row][32 columns], 8-byte piece g of row r at g ^ ((r >> 2) & 7)
+        // k-blocked C: staged as [block j][row][32 columns], 8-byte piece g of row r at g ^ ((r >> 1) & 7)
+        // (of the XOR functions measured, the one with the fewest bank conflicts: about 0.3 % of the
+        // launch's CU-cycles, against 0.6 % with (r >> 2) & 7)
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)((long)N * c_cap * 2),
                                                                                0x00020000);
 #pragma unroll
@@ -535,11 +538,11 @@ __device__ __forceinline__ void store_tile32s_lds(f32x16 (&acc)[TM][TN], void* C
                     const int g = 2 * p + hl;
                     const u2 pk = {pack_bf16x2(silu_f32(acc[i][j][4 * p]), silu_f32(acc[i][j][4 * p + 1])),
                                    pack_bf16x2(silu_f32(acc[i][j][4 * p + 2]), silu_f32(acc[i][j][4 * p + 3]))};
-                    *(lds_u2*)(st + (j * 32 + r) * 64 + (g ^ ((r >> 2) & 7)) * 8) = pk;
+                    *(lds_u2*)(st + (j * 32 + r) * 64 + (g ^ ((r >> 1) & 7)) * 8) = pk;
                 }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int j = k >> 1, rr = (k & 1) * 16 + (l >> 2), q = l & 3, f = (rr >> 2) & 7;
+                const int j = k >> 1, rr = (k & 1) * 16 + (l >> 2), q = l & 3, f = (rr >> 1) & 7;
                 const u2 lo = *(lds_u2*)(st + (j * 32 + rr) * 64 + ((2 * q) ^ f) * 8);
                 const u2 hi = *(lds_u2*)(st + (j * 32 + rr) * 64 + ((2 * q + 1) ^ f) * 8);
                 const int rowrel = wm * WTM + i * 32 + rr, col = n0 + wn * WTN + j * 32;
@@ -597,16 +600,15 @@ __device__ __forceinline__ void store_tile32s_lds(f32x16 (&acc)[TM][TN], void* C
             if (word)
                 __builtin_amdgcn_raw_buffer_store_b32(
                     sw, rs_s, (l < 32 && n0 + wn * WTN < N) ? rowrel * lds_sc + (wn * WTN) / 32 : 0x7ffffff0, 0, 0);
+            // 8 bytes per lane, so that the 16 lanes of an LDS pass read 16 distinct banks' pieces of one row;
+            // each store still writes 2 whole rows of 256 bytes
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int rr = 4 * k + (l >> 4), q = l & 15;
-                const u2 lo = *(lds_u2*)(st + rr * 256 + ((2 * q) ^ rr) * 8);
-                const u2 hi = *(lds_u2*)(st + rr * 256 + ((2 * q + 1) ^ rr) * 8);
-                const int rrel = wm * WTM + i * 32 + rr, colrel = wn * WTN + 8 * q;
+            for (int k = 0; k < 16; ++k) {
+                const int rr = 2 * k + (l >> 5), pc = l & 31;
+                const u2 v = *(lds_u2*)(st + rr * 256 + (pc ^ rr) * 8);
+                const int rrel = wm * WTM + i * 32 + rr, colrel = wn * WTN + 4 * pc;
                 const int off = n0 + colrel < N ? (rrel * (int)ldc + colrel) * 2 : 0x7ffffff0;
-                typedef __attribute__((ext_vector_type(4))) unsigned u4;
-                const u4 v = {lo[0], lo[1], hi[0], hi[1]};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rs_v, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(v, rs_v, off, 0, 0);
             }
         }
     }
