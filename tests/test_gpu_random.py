@@ -1,9 +1,10 @@
 """Seeded random-shape GPU parity sweep.
 
-Forty layers with shapes drawn from a fixed seed (tokens, widths, expert
-counts, top-k, drop threshold, skewed router bias, shared expert, fp32 or
-bf16) run through every entry point the shape admits, each against the
-oracle:
+Fifty-six layers with shapes drawn from fixed seeds (forty of any shape:
+tokens, widths, expert counts, top-k, drop threshold, skewed router bias,
+shared expert, fp32 or bf16; eight whose shared expert runs inside the routed
+launches; eight on the 256x256 tiles with ragged widths) run through every
+entry point the shape admits, each against the oracle:
 * moe_forward and the step-wise route -> permute -> grouped_ffn -> combine;
 * moe_forward_fp8 (weights-only fp8) when H, F are multiples of 64 and >= 128;
 * moe_forward_mxfp8 (MX tokens and weights) when H, F are multiples of 128;
@@ -65,7 +66,26 @@ def _draw_shared_merged(n=8, seed=2025):
     return out
 
 
-CONFIGS = _draw_configs(40) + _draw_shared_merged(8)
+def _draw_large_tiles(n=8, seed=2026):
+    """bf16 layers on the 256x256 tiles (T*k/E >= 96) with widths that are multiples of 8 but not always of 32 or
+    128: partial N-tiles and rows past each expert in every epilogue form the large tiles store through LDS (fp32
+    y_perm, SiLU + bf16 h, block-scaled fp16 with word or byte scale stores)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        T = int(rng.integers(max(2, 100 * E // k), 2500))
+        H = int(rng.choice([32 * int(rng.integers(2, 33)), 8 * int(rng.integers(8, 130))]))
+        F = int(rng.choice([32 * int(rng.integers(2, 33)), 8 * int(rng.integers(8, 130))]))
+        drop = float(rng.choice([0.0, 0.1])) if k > 1 else 0.0
+        Fs = int(rng.choice([0, 0, 64]))
+        out.append(dict(T=T, H=H, F=F, E=E, k=k, drop=min(drop, 1.0 / k), zipf=0.0, Fs=Fs, dtype="bf16",
+                        seed=3200 + i))
+    return out
+
+
+CONFIGS = _draw_configs(40) + _draw_shared_merged(8) + _draw_large_tiles(8)
 
 
 def _check_y(y_gpu, y_ref, tol=Y_TOL):
